@@ -1,0 +1,164 @@
+/*
+ * skv.h — streaming KV cache for chunk-causal video attention on MI355X (gfx950).
+ *
+ * C ABI of the hot path the LingBot-World 2.0 and ABot-World pages describe:
+ * a new latent chunk of c frames attends to a bounded KV cache that holds S
+ * never-evicted sink frames plus a sliding window of recent frames, with 3D
+ * rotary embeddings that carry time either as an absolute frame offset or as a
+ * relative slot index.  Pages cited below:
+ *   [LB-causal]   "LingBot-World 2.0因果预训练范式深度剖析" (sheratonhq.com)
+ *   [LB-fast]     "从40步到4步：LingBot-World 2.0实时推理蒸馏（causal_fast）原理与关键代码解读" (hmyw.cn)
+ *   [LB-src]      LingBot-World 2.0 wan/ source map (kwkr.cn)
+ *   [ABot-stream] "ABot-World流式因果推理深度解析：KV缓存与块级注意力如何让24小时连续生成不漂移" (lpnh.cn)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are [tokens, heads, head_dim], row-major, tokens frame-major and
+ *     row-major inside a latent frame of grid_h x grid_w tokens (F tokens).
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; it must be
+ *     16-byte aligned.  The library allocates only the small host-side handle.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues work on that stream and never synchronises, except
+ *     kv_cache_gather, which fills a host array from host state.
+ *   - Arguments are validated before anything is enqueued; on a validation error
+ *     nothing is enqueued and the handle is unchanged.  A failed HIP launch
+ *     returns SKV_ERR_HIP and poisons the handle: every later call on it returns
+ *     SKV_ERR_STATE until kv_cache_reset.
+ *   - Cache bookkeeping lives on the host and advances at enqueue time, so calls
+ *     on one handle must be issued in order on one stream.  A handle is not
+ *     thread-safe; separate handles are independent (one handle per layer).
+ */
+#ifndef SKV_H
+#define SKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKV_ABI_VERSION 1
+
+typedef enum {
+  SKV_OK = 0,
+  SKV_ERR_NULL = 1,    /* a required pointer is NULL */
+  SKV_ERR_CONFIG = 2,  /* invalid or unsupported configuration */
+  SKV_ERR_SHAPE = 3,   /* n_frames / token counts out of range */
+  SKV_ERR_ALIGN = 4,   /* a tensor pointer is not 16-byte aligned */
+  SKV_ERR_STATE = 5,   /* call not valid in the handle's state (or poisoned handle) */
+  SKV_ERR_HIP = 6      /* a HIP launch or runtime call failed */
+} skv_status;
+
+typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
+
+/* Time axis of the rotary embedding.
+ *   ABS: frame f's key is stored already rotated at time id f; a chunk starting
+ *        at frame s rotates its queries/keys at ids s..s+c-1 ([LB-src] 改造③,
+ *        rope_apply(..., start_frame)).
+ *   REL: the cache stores un-rotated keys (k_raw); each chunk rotates only the
+ *        visible window, at time id = slot index in the visible sequence, clamped
+ *        to [0, window_frames-1] ([ABot-stream] 机制三). */
+typedef enum { SKV_ROPE_ABS = 0, SKV_ROPE_REL = 1 } skv_rope_mode;
+
+typedef struct {
+  int32_t heads, head_dim;      /* H, D.  bf16: D in {64, 128}; f32: D in {32, 64, 128} */
+  int32_t grid_h, grid_w;       /* F = grid_h * grid_w tokens per latent frame */
+  int32_t chunk_frames;         /* c >= 1: frames per generated chunk */
+  int32_t sink_frames;          /* S >= 0: first frames never evicted */
+  int32_t window_frames;        /* W >= S + c: frames visible to a chunk, sinks and chunk included */
+  int32_t rope_t, rope_h, rope_w; /* head_dim split; 0,0,0 -> D-4*(D/6), 2*(D/6), 2*(D/6); each even, sum D */
+  double rope_theta;            /* rotary base; 0 -> 10000 */
+  int32_t rope_mode;            /* skv_rope_mode */
+  int32_t dtype;                /* skv_dtype of every tensor the handle touches */
+} skv_config;
+
+typedef struct {
+  int64_t n_appended;   /* frames appended since init/reset (T) */
+  int32_t n_cached;     /* frames the cache holds now */
+  int32_t n_sink_vis;   /* sink frames a chunk of c frames would see now */
+  int32_t n_ring_vis;   /* non-sink history frames it would see */
+  int32_t n_vis;        /* n_sink_vis + n_ring_vis + c */
+  int32_t ring_start;   /* physical slot of the oldest visible non-sink frame (-1 if none) */
+  int32_t window_ready; /* REL: 1 if rope_apply_window ran since the last append/reset */
+  int32_t poisoned;     /* 1 after a failed launch, until kv_cache_reset */
+} kv_cache_info_t;
+
+typedef struct skv_cache skv_cache; /* opaque host-side handle */
+
+/* ABI version (SKV_ABI_VERSION) and a static message for a status code. */
+int skv_abi_version(void);
+const char* skv_status_string(skv_status s);
+
+/* Bytes the caller must allocate for one K store and one V store (each
+ * W*F*H*D elements of cfg->dtype) and for the REL window workspace
+ * ((W-c)*F*H*D elements; 0 in ABS mode).  Physical layout of a store:
+ * [H][W*F][D] (head-major); slot s holds tokens [s*F, (s+1)*F).  Frame f < S
+ * lives in slot f, frame f >= S in slot S + (f-S) mod (W-S). */
+skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_t* workspace_bytes);
+
+/* Bind caller-allocated stores (and, in REL mode, the workspace) to a new
+ * handle with zero frames appended ([ABot-stream] reset_stream()).  The device
+ * memory is not touched.  *out receives the handle. */
+skv_status kv_cache_init(const skv_config* cfg, void* k_store, void* v_store, void* workspace,
+                         skv_cache** out);
+
+/* Forget every frame (counters to zero) and clear the poisoned flag. */
+skv_status kv_cache_reset(skv_cache* cache);
+
+/* Free the host handle (device memory stays the caller's). NULL is a no-op. */
+skv_status kv_cache_destroy(skv_cache* cache);
+
+/* Write back n_frames clean frames ([LB-fast] 3. KV 缓存 滚动窗口; [ABot-stream]
+ * 机制二 clean-context write-back).  k, v: [n_frames*F, H, D].  ABS: k must be
+ * the rotated keys; REL: the raw keys.  Frames go to their ring slots; a frame
+ * written to a ring slot evicts the frame that held it, which is the oldest
+ * non-sink frame, so the logical cache is exactly the one the pages obtain by
+ * shifting the post-sink entries left.  Requires 1 <= n_frames <= W - S. */
+skv_status kv_cache_append_evict(skv_cache* cache, const void* k, const void* v, int32_t n_frames,
+                                 void* stream);
+
+/* 3D rotary embedding of x_in [n_frames*F, H, D] into x_out (may alias x_in).
+ * Token (frame i, row r, col w) is rotated at positions (t_i, r, w): head_dim
+ * is split [time | height | width] and each adjacent pair (x_2k, x_2k+1) turns
+ * by position * theta^(-2k/d_axis).  ABS: t_i = start_frame + i (start_frame >= 0).
+ * REL: n_frames must equal c and t_i = n_vis - c + i (the chunk's slots);
+ * start_frame is ignored.  fp32 arithmetic, angles reduced in fp64. */
+skv_status rope_apply(const skv_cache* cache, const void* x_in, void* x_out, int32_t n_frames,
+                      int64_t start_frame, void* stream);
+
+/* REL only: rotate the visible history k_raw (sinks, then the visible ring
+ * frames oldest first) at time ids 0..n_vis-c-1 into the workspace, once per
+ * chunk; its result serves every pass until the next append or reset. */
+skv_status rope_apply_window(skv_cache* cache, void* stream);
+
+/* Chunk attention ([LB-fast] 3. KV 缓存 滚动窗口: attention over the window
+ * slice; [ABot-stream] 机制二: block-causal, frames of a chunk see each other).
+ * q, k_cur, v_cur: [c*F, H, D], q and k_cur already rotated with rope_apply.
+ * out[i] = softmax(q_i . K^T / sqrt(D)) V over the visible keys: the visible
+ * sink frames, the visible ring frames, and the current chunk.  The cache is
+ * read only.  fp32 softmax and accumulation; out in cfg dtype.  n_frames must
+ * equal c.  REL mode with cached history requires rope_apply_window first. */
+skv_status chunk_attention(const skv_cache* cache, const void* q, const void* k_cur, const void* v_cur,
+                           int32_t n_frames, void* out, void* stream);
+
+/* Cross attention over cached text K/V ([LB-causal] CrossAttention_KVCache;
+ * [ABot-stream] 512 text tokens computed once): out = softmax(q K_text^T / sqrt(D)) V_text,
+ * no rotary embedding, no mask.  q/out [n_q, H, D]; k_text/v_text [n_text, H, D].
+ * Independent of any cache handle (a prompt swap keeps the KV history). */
+skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const void* v_text,
+                           int32_t n_text, int32_t heads, int32_t head_dim, int32_t dtype, void* out,
+                           void* stream);
+
+/* Host-side bookkeeping of the handle. */
+skv_status kv_cache_info(const skv_cache* cache, kv_cache_info_t* info);
+
+/* Logical snapshot: copy the cached frames oldest first (sinks, then ring in
+ * append order) into k_out/v_out [n_cached*F, H, D] (device) and their frame
+ * ids into frame_ids_host[n_cached] (host; may be NULL).  Enqueued on stream. */
+skv_status kv_cache_gather(const skv_cache* cache, void* k_out, void* v_out, int64_t* frame_ids_host,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SKV_H */

@@ -1,0 +1,245 @@
+"""Python binding of ``libskv.so`` (C ABI in ``include/skv.h``): argument marshalling only.
+
+Every step of the hot path runs in the library's HIP kernels.  torch is used for
+device memory (the stores, the workspace, inputs and outputs) and for the
+current HIP stream.  Importing this package fails loudly when the library has
+not been built (``python -m streaming_kv_cache_amd.build``); there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
+
+OK, ERR_NULL, ERR_CONFIG, ERR_SHAPE, ERR_ALIGN, ERR_STATE, ERR_HIP = range(7)
+F32, BF16 = 0, 1
+ROPE_ABS, ROPE_REL = 0, 1
+
+EXPORTED = (
+    "skv_abi_version", "skv_status_string", "kv_cache_bytes", "kv_cache_init", "kv_cache_reset",
+    "kv_cache_destroy", "kv_cache_append_evict", "rope_apply", "rope_apply_window", "chunk_attention",
+    "cross_attention", "kv_cache_info", "kv_cache_gather",
+)
+
+
+class SkvConfig(ctypes.Structure):
+    _fields_ = [
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+        ("chunk_frames", ctypes.c_int32), ("sink_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
+        ("rope_t", ctypes.c_int32), ("rope_h", ctypes.c_int32), ("rope_w", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+        ("rope_mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+class KvCacheInfo(ctypes.Structure):
+    _fields_ = [
+        ("n_appended", ctypes.c_int64), ("n_cached", ctypes.c_int32), ("n_sink_vis", ctypes.c_int32),
+        ("n_ring_vis", ctypes.c_int32), ("n_vis", ctypes.c_int32), ("ring_start", ctypes.c_int32),
+        ("window_ready", ctypes.c_int32), ("poisoned", ctypes.c_int32),
+    ]
+
+
+class SkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m streaming_kv_cache_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "skv_abi_version": ([], ctypes.c_int),
+        "skv_status_string": ([st], ctypes.c_char_p),
+        "kv_cache_bytes": ([ctypes.POINTER(SkvConfig), ctypes.POINTER(ctypes.c_size_t),
+                            ctypes.POINTER(ctypes.c_size_t)], st),
+        "kv_cache_init": ([ctypes.POINTER(SkvConfig), vp, vp, vp, ctypes.POINTER(vp)], st),
+        "kv_cache_reset": ([vp], st),
+        "kv_cache_destroy": ([vp], st),
+        "kv_cache_append_evict": ([vp, vp, vp, i32, vp], st),
+        "rope_apply": ([vp, vp, vp, i32, i64, vp], st),
+        "rope_apply_window": ([vp, vp], st),
+        "chunk_attention": ([vp, vp, vp, vp, i32, vp, vp], st),
+        "cross_attention": ([vp, i32, vp, vp, i32, i32, i32, i32, vp, vp], st),
+        "kv_cache_info": ([vp, ctypes.POINTER(KvCacheInfo)], st),
+        "kv_cache_gather": ([vp, vp, vp, ctypes.POINTER(ctypes.c_int64), vp], st),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.skv_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise SkvError(status, where)
+
+
+def _stream(stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+@dataclass(frozen=True)
+class Config:
+    """Mirror of ``skv_config``.  Rotary split 0/0/0 and theta 0 select the defaults."""
+    heads: int
+    head_dim: int
+    grid_h: int
+    grid_w: int
+    chunk_frames: int
+    sink_frames: int
+    window_frames: int
+    rope_mode: int = ROPE_ABS
+    dtype: int = BF16
+    rope_split: tuple = (0, 0, 0)
+    rope_theta: float = 0.0
+
+    @property
+    def tokens_per_frame(self) -> int:
+        return self.grid_h * self.grid_w
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPE[self.dtype]
+
+    def c_struct(self) -> SkvConfig:
+        t, h, w = self.rope_split
+        return SkvConfig(self.heads, self.head_dim, self.grid_h, self.grid_w, self.chunk_frames,
+                         self.sink_frames, self.window_frames, t, h, w, float(self.rope_theta),
+                         int(self.rope_mode), int(self.dtype))
+
+
+def cache_bytes(cfg: Config):
+    """(bytes of one store, bytes of the REL workspace) for ``cfg``."""
+    c = cfg.c_struct()
+    s, w = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.kv_cache_bytes(ctypes.byref(c), ctypes.byref(s), ctypes.byref(w)), "kv_cache_bytes")
+    return s.value, w.value
+
+
+class KVCache:
+    """One layer's streaming KV cache: device stores owned here (torch), bookkeeping in the library."""
+
+    def __init__(self, cfg: Config, device="cuda"):
+        self.cfg = cfg
+        store, ws = cache_bytes(cfg)
+        self.k_store = torch.empty(store, dtype=torch.uint8, device=device)
+        self.v_store = torch.empty(store, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
+        h = ctypes.c_void_p()
+        c = cfg.c_struct()
+        _check(lib.kv_cache_init(ctypes.byref(c), _ptr(self.k_store), _ptr(self.v_store),
+                                 _ptr(self.workspace), ctypes.byref(h)), "kv_cache_init")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.kv_cache_destroy(h)
+            self._h = None
+
+    # -- argument checks (shape/dtype/device/contiguity); the library checks the rest
+    def _tensor(self, x: torch.Tensor, n_frames: int, name: str) -> torch.Tensor:
+        cfg = self.cfg
+        want = (n_frames * cfg.tokens_per_frame, cfg.heads, cfg.head_dim)
+        if tuple(x.shape) != want:
+            raise ValueError(f"{name}: expected shape {want}, got {tuple(x.shape)}")
+        if x.dtype != cfg.torch_dtype or not x.is_cuda or not x.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous {cfg.torch_dtype} CUDA tensor")
+        return x
+
+    def reset(self) -> None:
+        _check(lib.kv_cache_reset(self._h), "kv_cache_reset")
+
+    def info(self) -> KvCacheInfo:
+        i = KvCacheInfo()
+        _check(lib.kv_cache_info(self._h, ctypes.byref(i)), "kv_cache_info")
+        return i
+
+    def append_evict(self, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+        n = k.shape[0] // self.cfg.tokens_per_frame
+        self._tensor(k, n, "k")
+        self._tensor(v, n, "v")
+        _check(lib.kv_cache_append_evict(self._h, _ptr(k), _ptr(v), n, _stream(stream)), "kv_cache_append_evict")
+
+    def rope_apply(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, start_frame: int = 0,
+                   stream=None) -> torch.Tensor:
+        n = x.shape[0] // self.cfg.tokens_per_frame
+        self._tensor(x, n, "x")
+        out = torch.empty_like(x) if out is None else self._tensor(out, n, "out")
+        _check(lib.rope_apply(self._h, _ptr(x), _ptr(out), n, int(start_frame), _stream(stream)), "rope_apply")
+        return out
+
+    def rope_apply_window(self, stream=None) -> None:
+        _check(lib.rope_apply_window(self._h, _stream(stream)), "rope_apply_window")
+
+    def chunk_attention(self, q: torch.Tensor, k_cur: torch.Tensor, v_cur: torch.Tensor,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        c = self.cfg.chunk_frames
+        self._tensor(q, c, "q")
+        self._tensor(k_cur, c, "k_cur")
+        self._tensor(v_cur, c, "v_cur")
+        out = torch.empty_like(q) if out is None else self._tensor(out, c, "out")
+        _check(lib.chunk_attention(self._h, _ptr(q), _ptr(k_cur), _ptr(v_cur), c, _ptr(out), _stream(stream)),
+               "chunk_attention")
+        return out
+
+    def gather(self, stream=None):
+        """Logical cache contents (oldest first) and frame ids: (k, v, ids)."""
+        n = self.info().n_cached
+        cfg = self.cfg
+        shape = (n * cfg.tokens_per_frame, cfg.heads, cfg.head_dim)
+        k = torch.empty(shape, dtype=cfg.torch_dtype, device=self.k_store.device)
+        v = torch.empty_like(k)
+        ids = (ctypes.c_int64 * max(n, 1))()
+        if n:
+            _check(lib.kv_cache_gather(self._h, _ptr(k), _ptr(v), ids, _stream(stream)), "kv_cache_gather")
+        return k, v, [int(ids[i]) for i in range(n)]
+
+
+def cross_attention(q: torch.Tensor, k_text: torch.Tensor, v_text: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """softmax(q K_text^T / sqrt(D)) V_text per head; tensors [tokens, H, D] on the GPU."""
+    if q.dim() != 3 or k_text.dim() != 3 or k_text.shape != v_text.shape or q.shape[1:] != k_text.shape[1:]:
+        raise ValueError("q [n_q, H, D] and k_text/v_text [n_text, H, D] expected")
+    for t in (q, k_text, v_text):
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("contiguous CUDA tensors of one dtype expected")
+    out = torch.empty_like(q) if out is None else out
+    _check(lib.cross_attention(_ptr(q), q.shape[0], _ptr(k_text), _ptr(v_text), k_text.shape[0], q.shape[1],
+                               q.shape[2], _dtype_code(q.dtype), _ptr(out), _stream(stream)), "cross_attention")
+    return out

@@ -1,0 +1,200 @@
+// Cache update, logical gather and 3D rotary kernels (gfx950).
+//
+// All three are HBM-bound streaming kernels.  Work is organised by token: a
+// block owns a few tokens and its threads sweep the H*D elements of each token
+// in 16-byte vectors, so every global access is a run of at least D*elt
+// contiguous bytes on both the read and the write side, and index math per
+// vector is a shift and a mask.
+#include "skv_device.hpp"
+#include "skv_kernels.hpp"
+
+namespace skv {
+
+// ---------------------------------------------------------------- frame copy
+// Copies whole frames between two token views, for K and V at once
+// (blockIdx.y selects the tensor).  Used by
+//   * kv_cache_append_evict: caller's token-major chunk -> ring slots of the
+//     head-major stores ([LB-fast] 3. KV 缓存 滚动窗口: write the clean chunk;
+//     the ring slot of a frame is the one its evicted predecessor held), and
+//   * kv_cache_gather: ring slots -> logical (oldest first) token-major copy.
+constexpr int kCopyTokPerBlock = 4;
+constexpr int kCopyThreads = 256;
+
+struct CopyArgs {
+  TokView src[2], dst[2];
+  FrameRun runs[3];
+  int32_t nruns;
+  int32_t F, H, row_vec_shift;  // vectors per (token, head) row = 1 << row_vec_shift
+  int32_t elt;
+  int32_t n_tok;                // tokens in the launch
+};
+
+__global__ __launch_bounds__(kCopyThreads) void copy_frames_kernel(CopyArgs a) {
+  const int which = blockIdx.y;
+  const char* src = (const char*)a.src[which].base;
+  char* dst = (char*)a.dst[which].base;
+  const int64_t s_ts = a.src[which].tok_stride * a.elt, s_hs = a.src[which].head_stride * a.elt;
+  const int64_t d_ts = a.dst[which].tok_stride * a.elt, d_hs = a.dst[which].head_stride * a.elt;
+  const int row_vecs = 1 << a.row_vec_shift;
+  const int per_tok = a.H << a.row_vec_shift;
+  for (int tl = 0; tl < kCopyTokPerBlock; ++tl) {
+    const int gt = blockIdx.x * kCopyTokPerBlock + tl;  // token index in the launch
+    if (gt >= a.n_tok) break;
+    const int fi = gt / a.F, tok = gt - fi * a.F;      // launch frame, token in frame
+    int sf = 0, df = 0;
+    for (int r = 0; r < a.nruns; ++r) {
+      const FrameRun run = a.runs[r];
+      if (fi >= run.start && fi < run.start + run.count) {
+        sf = run.src0 + (fi - run.start);
+        df = run.dst0 + (fi - run.start);
+      }
+    }
+    const char* s_tok = src + (int64_t)(sf * a.F + tok) * s_ts;
+    char* d_tok = dst + (int64_t)(df * a.F + tok) * d_ts;
+    for (int t = threadIdx.x; t < per_tok; t += kCopyThreads) {
+      const int h = t >> a.row_vec_shift, c = t & (row_vecs - 1);
+      const u32x4_t v = *(const u32x4_t*)(s_tok + h * s_hs + c * 16);
+      *(u32x4_t*)(d_tok + h * d_hs + c * 16) = v;
+    }
+  }
+}
+
+hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], const FrameRun* runs, int nruns,
+                              int n_frames, int F, int H, int D, int elt, hipStream_t stream) {
+  CopyArgs a;
+  for (int i = 0; i < 2; ++i) {
+    a.src[i] = src[i];
+    a.dst[i] = dst[i];
+  }
+  for (int i = 0; i < 3; ++i) a.runs[i] = i < nruns ? runs[i] : FrameRun{0, 0, 0, 0};
+  a.nruns = nruns;
+  a.F = F;
+  a.H = H;
+  int row_vecs = D * elt / 16, sh = 0;
+  while ((1 << sh) < row_vecs) ++sh;
+  a.row_vec_shift = sh;
+  a.elt = elt;
+  a.n_tok = n_frames * F;
+  dim3 grid((a.n_tok + kCopyTokPerBlock - 1) / kCopyTokPerBlock, 2);
+  hipLaunchKernelGGL(copy_frames_kernel, grid, dim3(kCopyThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- 3D RoPE
+// [LB-src] 改造③ / [LB-causal] "Attention Sink" (start_frame offset) and
+// [ABot-stream] 机制三 (relative ids over the visible window): token (frame i,
+// row r, col w) turns pair k of the [time | height | width] part of head_dim by
+// position * omega_k.  cos/sin are computed once per (token, pair) in fp64 and
+// reused for every head; the rotation itself is fp32.
+constexpr int kRopeThreads = 256;
+
+struct RopeArgs {
+  TokView src, dst;
+  FrameRun runs[3];
+  int32_t nruns;
+  int32_t F, gw, H, D;
+  int64_t t0;          // time id of launch frame 0 (before clamping)
+  int32_t clamp_max;   // >= 0: clamp time ids to [0, clamp_max]
+  int32_t pair_h, pair_w;  // first pair index of the height / width parts
+  int32_t n_tok;
+  double omega[64];    // per pair, theta^(-2k/d_axis) with k counted inside its axis
+};
+
+template <typename T>
+__device__ __forceinline__ void rope_row(const T* __restrict__ s, T* __restrict__ d, const float (&cs)[4],
+                                         const float (&sn)[4]);
+
+template <>
+__device__ __forceinline__ void rope_row<float>(const float* __restrict__ s, float* __restrict__ d,
+                                                const float (&cs)[4], const float (&sn)[4]) {
+  const f32x4_t a = *(const f32x4_t*)s, b = *(const f32x4_t*)(s + 4);
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  float y[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    y[2 * p] = x[2 * p] * cs[p] - x[2 * p + 1] * sn[p];
+    y[2 * p + 1] = x[2 * p] * sn[p] + x[2 * p + 1] * cs[p];
+  }
+  *(f32x4_t*)d = f32x4_t{y[0], y[1], y[2], y[3]};
+  *(f32x4_t*)(d + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
+}
+
+template <>
+__device__ __forceinline__ void rope_row<__bf16>(const __bf16* __restrict__ s, __bf16* __restrict__ d,
+                                                 const float (&cs)[4], const float (&sn)[4]) {
+  const u32x4_t w = *(const u32x4_t*)s;
+  u32x4_t o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float x0 = bf16_lo_to_f32(w[p]), x1 = bf16_hi_to_f32(w[p]);
+    o[p] = pack_bf16x2(x0 * cs[p] - x1 * sn[p], x0 * sn[p] + x1 * cs[p]);
+  }
+  *(u32x4_t*)d = o;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeArgs a) {
+  const int G = a.D >> 3;                 // groups of 4 pairs (8 elements) per row
+  const int tpb = kRopeThreads / G;       // tokens per block
+  const int g = threadIdx.x % G, tl = threadIdx.x / G;
+  const int gt = blockIdx.x * tpb + tl;   // token index in the launch
+  if (gt >= a.n_tok) return;
+  const int fi = gt / a.F, tok = gt - fi * a.F;
+  int sf = 0, df = 0;
+  for (int r = 0; r < a.nruns; ++r) {
+    const FrameRun run = a.runs[r];
+    if (fi >= run.start && fi < run.start + run.count) {
+      sf = run.src0 + (fi - run.start);
+      df = run.dst0 + (fi - run.start);
+    }
+  }
+  int64_t t = a.t0 + fi;
+  if (a.clamp_max >= 0) t = t < 0 ? 0 : (t > a.clamp_max ? a.clamp_max : t);
+  const int row = tok / a.gw, col = tok - row * a.gw;
+  float cs[4], sn[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int pair = g * 4 + p;
+    const double pos = pair < a.pair_h ? (double)t : (pair < a.pair_w ? (double)row : (double)col);
+    double sd, cd;
+    sincos(pos * a.omega[pair], &sd, &cd);
+    cs[p] = (float)cd;
+    sn[p] = (float)sd;
+  }
+  const T* s = (const T*)a.src.base + (int64_t)(sf * a.F + tok) * a.src.tok_stride + g * 8;
+  T* d = (T*)a.dst.base + (int64_t)(df * a.F + tok) * a.dst.tok_stride + g * 8;
+  for (int h = 0; h < a.H; ++h) rope_row<T>(s + h * a.src.head_stride, d + h * a.dst.head_stride, cs, sn);
+}
+
+hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream) {
+  RopeArgs a;
+  a.src = L.src;
+  a.dst = L.dst;
+  for (int i = 0; i < 3; ++i) a.runs[i] = i < L.nruns ? L.runs[i] : FrameRun{0, 0, 0, 0};
+  a.nruns = L.nruns;
+  a.F = L.F;
+  a.gw = L.gw;
+  a.H = L.H;
+  a.D = L.D;
+  a.t0 = L.t0;
+  a.clamp_max = L.clamp_max;
+  a.pair_h = L.rope_t / 2;
+  a.pair_w = (L.rope_t + L.rope_h) / 2;
+  a.n_tok = L.n_frames * L.F;
+  // omega_k = theta^(-2k/d_axis), k counted from 0 inside each axis
+  const int dims[3] = {L.rope_t, L.rope_h, L.rope_w};
+  int p = 0;
+  for (int ax = 0; ax < 3; ++ax)
+    for (int k = 0; k < dims[ax] / 2; ++k) a.omega[p++] = pow(L.theta, -2.0 * k / (double)dims[ax]);
+  for (; p < 64; ++p) a.omega[p] = 0.0;
+  const int G = L.D / 8;
+  const int tpb = kRopeThreads / G;
+  dim3 grid((a.n_tok + tpb - 1) / tpb);
+  if (L.dtype_bf16)
+    hipLaunchKernelGGL(rope_kernel<__bf16>, grid, dim3(kRopeThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(kRopeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -1,0 +1,68 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16
+// conversion, and the argument blocks the host fills.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 <-> f32.  Widening is exact; narrowing rounds to nearest even.
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// One run of frames for the frame-copy and rotary kernels: frames
+// [start, start+count) of the launch read source frame src0+(i-start) and
+// write destination frame dst0+(i-start).
+struct FrameRun {
+  int32_t start, count, src0, dst0;
+};
+
+// Strided view of a [frames*F tokens, H, D] tensor:
+// element (token t, head h, d) is at base + t*tok_stride + h*head_stride + d.
+struct TokView {
+  void* base;
+  int64_t tok_stride, head_stride;
+};
+
+// One contiguous range of visible keys for the attention kernels.
+// key j of the range, head h: K at k + j*k_rs + h*k_hs, V at v + j*v_rs + h*v_hs.
+struct KvSeg {
+  const void* k;
+  const void* v;
+  int64_t k_hs, k_rs, v_hs, v_rs;
+  int32_t n, pad_;
+};
+
+struct AttnArgs {
+  const void* q;   // [Lq, H, D]
+  void* out;       // [Lq, H, D]
+  KvSeg seg[4];
+  int32_t nseg;
+  int32_t Lq, H;
+  float sl2;       // softmax scale * log2(e)
+};
+
+// Bijective remap of a workgroup id so that workgroups the dispatcher sends to
+// the same XCD (ids congruent mod 8) work on consecutive tiles.
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int xcd = pid & 7, idx = pid >> 3;
+  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+}  // namespace skv

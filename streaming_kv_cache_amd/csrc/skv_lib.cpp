@@ -1,0 +1,342 @@
+// C ABI of the streaming KV cache (include/skv.h): argument checks, host-side
+// ring bookkeeping and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <new>
+
+#include "../../include/skv.h"
+#include "skv_core.hpp"
+#include "skv_kernels.hpp"
+
+struct skv_cache {
+  skv::Geometry g;
+  skv::RingState ring;
+  void* k_store = nullptr;
+  void* v_store = nullptr;
+  void* ws = nullptr;
+  bool window_ready = false;
+  bool poisoned = false;
+};
+
+namespace {
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+skv_status check_ptr(const void* p) {
+  if (!p) return SKV_ERR_NULL;
+  if (misaligned(p)) return SKV_ERR_ALIGN;
+  return SKV_OK;
+}
+
+skv_status check_handle(const skv_cache* c) {
+  if (!c) return SKV_ERR_NULL;
+  if (c->poisoned) return SKV_ERR_STATE;
+  return SKV_OK;
+}
+
+skv_status launched(skv_cache* c, hipError_t e) {
+  if (e == hipSuccess) return SKV_OK;
+  if (c) c->poisoned = true;
+  return SKV_ERR_HIP;
+}
+
+const char* byte_ptr(const void* base, int64_t elems, int elt) { return (const char*)base + elems * elt; }
+
+// Head-major store view: token t of slot-space, head h at (h*W*F + t)*D.
+skv::TokView store_view(const skv::Geometry& g, void* base) {
+  return skv::TokView{base, (int64_t)g.D, (int64_t)g.W * g.F * g.D};
+}
+// Caller's token-major [tokens, H, D] view.
+skv::TokView token_view(const skv::Geometry& g, const void* base) {
+  return skv::TokView{const_cast<void*>(base), (int64_t)g.H * g.D, (int64_t)g.D};
+}
+
+float softmax_scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
+
+}  // namespace
+
+extern "C" {
+
+int skv_abi_version(void) { return SKV_ABI_VERSION; }
+
+const char* skv_status_string(skv_status s) {
+  switch (s) {
+    case SKV_OK: return "ok";
+    case SKV_ERR_NULL: return "null pointer";
+    case SKV_ERR_CONFIG: return "invalid or unsupported configuration";
+    case SKV_ERR_SHAPE: return "frame or token count out of range";
+    case SKV_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case SKV_ERR_STATE: return "call not valid in the cache's state (or cache poisoned by a failed launch)";
+    case SKV_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_t* workspace_bytes) {
+  if (!cfg || !store_bytes_each || !workspace_bytes) return SKV_ERR_NULL;
+  skv::Geometry g;
+  skv_status st = skv::make_geometry(cfg, &g);
+  if (st != SKV_OK) return st;
+  *store_bytes_each = (size_t)skv::store_elems(g) * g.elt;
+  *workspace_bytes = (size_t)skv::workspace_elems(g) * g.elt;
+  return SKV_OK;
+}
+
+skv_status kv_cache_init(const skv_config* cfg, void* k_store, void* v_store, void* workspace, skv_cache** out) {
+  if (!cfg || !out) return SKV_ERR_NULL;
+  skv::Geometry g;
+  skv_status st = skv::make_geometry(cfg, &g);
+  if (st != SKV_OK) return st;
+  if ((st = check_ptr(k_store)) != SKV_OK) return st;
+  if ((st = check_ptr(v_store)) != SKV_OK) return st;
+  if (g.mode == SKV_ROPE_REL && (st = check_ptr(workspace)) != SKV_OK) return st;
+  skv_cache* c = new (std::nothrow) skv_cache();
+  if (!c) return SKV_ERR_STATE;
+  c->g = g;
+  c->k_store = k_store;
+  c->v_store = v_store;
+  c->ws = g.mode == SKV_ROPE_REL ? workspace : nullptr;
+  *out = c;
+  return SKV_OK;
+}
+
+skv_status kv_cache_reset(skv_cache* c) {
+  if (!c) return SKV_ERR_NULL;
+  c->ring.T = 0;
+  c->window_ready = false;
+  c->poisoned = false;
+  return SKV_OK;
+}
+
+skv_status kv_cache_destroy(skv_cache* c) {
+  delete c;
+  return SKV_OK;
+}
+
+skv_status kv_cache_info(const skv_cache* c, kv_cache_info_t* info) {
+  if (!c || !info) return SKV_ERR_NULL;
+  const skv::VisiblePlan p = c->ring.plan(c->g, c->g.c);
+  info->n_appended = c->ring.T;
+  info->n_cached = c->ring.n_cached(c->g);
+  info->n_sink_vis = p.n_sink_vis;
+  info->n_ring_vis = p.n_ring_vis;
+  info->n_vis = p.n_vis;
+  info->ring_start = p.ring_start;
+  info->window_ready = c->window_ready ? 1 : 0;
+  info->poisoned = c->poisoned ? 1 : 0;
+  return SKV_OK;
+}
+
+skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int32_t n_frames, void* stream) {
+  skv_status st = check_handle(c);
+  if (st != SKV_OK) return st;
+  if ((st = check_ptr(k)) != SKV_OK) return st;
+  if ((st = check_ptr(v)) != SKV_OK) return st;
+  const skv::Geometry& g = c->g;
+  if (n_frames < 1 || n_frames > g.W - g.S) return SKV_ERR_SHAPE;
+  // frames T .. T+n-1 -> their slots, merged into runs of consecutive slots
+  skv::FrameRun runs[3];
+  int nruns = 0;
+  for (int i = 0; i < n_frames; ++i) {
+    const int slot = c->ring.slot_of(g, c->ring.T + i);
+    if (nruns > 0 && runs[nruns - 1].dst0 + runs[nruns - 1].count == slot) {
+      ++runs[nruns - 1].count;
+    } else {
+      if (nruns == 3) return SKV_ERR_STATE;  // cannot happen for n <= W - S
+      runs[nruns++] = skv::FrameRun{i, 1, i, slot};
+    }
+  }
+  const skv::TokView src[2] = {token_view(g, k), token_view(g, v)};
+  const skv::TokView dst[2] = {store_view(g, c->k_store), store_view(g, c->v_store)};
+  st = launched(c, skv::launch_copy_frames(src, dst, runs, nruns, n_frames, g.F, g.H, g.D, g.elt,
+                                            (hipStream_t)stream));
+  if (st != SKV_OK) return st;
+  c->ring.T += n_frames;
+  c->window_ready = false;
+  return SKV_OK;
+}
+
+skv_status rope_apply(const skv_cache* cc, const void* x_in, void* x_out, int32_t n_frames, int64_t start_frame,
+                      void* stream) {
+  skv_cache* c = const_cast<skv_cache*>(cc);
+  skv_status st = check_handle(c);
+  if (st != SKV_OK) return st;
+  if ((st = check_ptr(x_in)) != SKV_OK) return st;
+  if ((st = check_ptr(x_out)) != SKV_OK) return st;
+  const skv::Geometry& g = c->g;
+  if (n_frames < 1 || (int64_t)n_frames * g.F > (int64_t)INT32_MAX / 2) return SKV_ERR_SHAPE;
+  skv::RopeLaunch L;
+  L.src = token_view(g, x_in);
+  L.dst = token_view(g, x_out);
+  L.runs[0] = skv::FrameRun{0, n_frames, 0, 0};
+  L.nruns = 1;
+  L.n_frames = n_frames;
+  L.F = g.F;
+  L.gw = g.gw;
+  L.H = g.H;
+  L.D = g.D;
+  L.rope_t = g.rope_t;
+  L.rope_h = g.rope_h;
+  L.rope_w = g.rope_w;
+  L.theta = g.theta;
+  L.dtype_bf16 = g.dtype == SKV_BF16;
+  if (g.mode == SKV_ROPE_ABS) {
+    if (start_frame < 0) return SKV_ERR_SHAPE;
+    L.t0 = start_frame;
+    L.clamp_max = -1;
+  } else {
+    if (n_frames != g.c) return SKV_ERR_SHAPE;
+    const skv::VisiblePlan p = c->ring.plan(g, g.c);
+    L.t0 = p.n_vis - g.c;
+    L.clamp_max = g.W - 1;
+  }
+  return launched(c, skv::launch_rope(L, (hipStream_t)stream));
+}
+
+skv_status rope_apply_window(skv_cache* c, void* stream) {
+  skv_status st = check_handle(c);
+  if (st != SKV_OK) return st;
+  const skv::Geometry& g = c->g;
+  if (g.mode != SKV_ROPE_REL) return SKV_ERR_STATE;
+  const skv::VisiblePlan p = c->ring.plan(g, g.c);
+  if (p.n_hist > 0) {
+    skv::RopeLaunch L;
+    L.src = store_view(g, c->k_store);
+    L.dst = skv::TokView{c->ws, (int64_t)g.D, (int64_t)(g.W - g.c) * g.F * g.D};
+    L.nruns = p.n_runs;
+    for (int i = 0; i < p.n_runs; ++i)
+      L.runs[i] = skv::FrameRun{p.runs[i].logical0, p.runs[i].frames, p.runs[i].slot0, p.runs[i].logical0};
+    L.n_frames = p.n_hist;
+    L.F = g.F;
+    L.gw = g.gw;
+    L.H = g.H;
+    L.D = g.D;
+    L.rope_t = g.rope_t;
+    L.rope_h = g.rope_h;
+    L.rope_w = g.rope_w;
+    L.theta = g.theta;
+    L.t0 = 0;
+    L.clamp_max = g.W - 1;
+    L.dtype_bf16 = g.dtype == SKV_BF16;
+    st = launched(c, skv::launch_rope(L, (hipStream_t)stream));
+    if (st != SKV_OK) return st;
+  }
+  c->window_ready = true;
+  return SKV_OK;
+}
+
+skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur, const void* v_cur,
+                           int32_t n_frames, void* out, void* stream) {
+  skv_cache* c = const_cast<skv_cache*>(cc);
+  skv_status st = check_handle(c);
+  if (st != SKV_OK) return st;
+  if ((st = check_ptr(q)) != SKV_OK) return st;
+  if ((st = check_ptr(k_cur)) != SKV_OK) return st;
+  if ((st = check_ptr(v_cur)) != SKV_OK) return st;
+  if ((st = check_ptr(out)) != SKV_OK) return st;
+  const skv::Geometry& g = c->g;
+  if (n_frames != g.c) return SKV_ERR_SHAPE;
+  const skv::VisiblePlan p = c->ring.plan(g, g.c);
+  const bool rel = g.mode == SKV_ROPE_REL;
+  if (rel && p.n_hist > 0 && !c->window_ready) return SKV_ERR_STATE;
+
+  skv::AttnArgs a;
+  a.q = q;
+  a.out = out;
+  a.Lq = g.c * g.F;
+  a.H = g.H;
+  a.sl2 = softmax_scale_log2(g.D);
+  a.nseg = 0;
+  const int64_t store_hs = (int64_t)g.W * g.F * g.D;
+  const int64_t ws_hs = (int64_t)(g.W - g.c) * g.F * g.D;
+  for (int i = 0; i < p.n_runs; ++i) {
+    const skv::SlotRun& r = p.runs[i];
+    skv::KvSeg sg;
+    const int64_t slot_off = (int64_t)r.slot0 * g.F * g.D;
+    if (rel) {
+      sg.k = byte_ptr(c->ws, (int64_t)r.logical0 * g.F * g.D, g.elt);
+      sg.k_hs = ws_hs;
+    } else {
+      sg.k = byte_ptr(c->k_store, slot_off, g.elt);
+      sg.k_hs = store_hs;
+    }
+    sg.k_rs = g.D;
+    sg.v = byte_ptr(c->v_store, slot_off, g.elt);
+    sg.v_hs = store_hs;
+    sg.v_rs = g.D;
+    sg.n = r.frames * g.F;
+    sg.pad_ = 0;
+    a.seg[a.nseg++] = sg;
+  }
+  skv::KvSeg cur;
+  cur.k = k_cur;
+  cur.v = v_cur;
+  cur.k_hs = g.D;
+  cur.k_rs = (int64_t)g.H * g.D;
+  cur.v_hs = g.D;
+  cur.v_rs = (int64_t)g.H * g.D;
+  cur.n = g.c * g.F;
+  cur.pad_ = 0;
+  a.seg[a.nseg++] = cur;
+  for (int i = a.nseg; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+  const hipError_t e = g.dtype == SKV_BF16 ? skv::launch_attention_bf16(a, g.D, (hipStream_t)stream)
+                                            : skv::launch_attention_f32(a, g.D, (hipStream_t)stream);
+  return launched(c, e);
+}
+
+skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const void* v_text, int32_t n_text,
+                           int32_t heads, int32_t head_dim, int32_t dtype, void* out, void* stream) {
+  skv_status st;
+  if ((st = check_ptr(q)) != SKV_OK) return st;
+  if ((st = check_ptr(k_text)) != SKV_OK) return st;
+  if ((st = check_ptr(v_text)) != SKV_OK) return st;
+  if ((st = check_ptr(out)) != SKV_OK) return st;
+  if (heads < 1 || heads > 4096) return SKV_ERR_CONFIG;
+  if (!skv::attention_head_dim_supported(dtype, head_dim)) return SKV_ERR_CONFIG;
+  if (n_q < 1 || n_text < 1 || (int64_t)n_text > (int64_t)INT32_MAX / 2 ||
+      (int64_t)n_q * heads > (int64_t)INT32_MAX / 2)
+    return SKV_ERR_SHAPE;
+  skv::AttnArgs a;
+  a.q = q;
+  a.out = out;
+  a.Lq = n_q;
+  a.H = heads;
+  a.sl2 = softmax_scale_log2(head_dim);
+  a.nseg = 1;
+  a.seg[0] = skv::KvSeg{k_text, v_text, (int64_t)head_dim, (int64_t)heads * head_dim,
+                        (int64_t)head_dim, (int64_t)heads * head_dim, n_text, 0};
+  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+  const hipError_t e = dtype == SKV_BF16 ? skv::launch_attention_bf16(a, head_dim, (hipStream_t)stream)
+                                         : skv::launch_attention_f32(a, head_dim, (hipStream_t)stream);
+  return e == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+}
+
+skv_status kv_cache_gather(const skv_cache* cc, void* k_out, void* v_out, int64_t* frame_ids_host, void* stream) {
+  skv_cache* c = const_cast<skv_cache*>(cc);
+  skv_status st = check_handle(c);
+  if (st != SKV_OK) return st;
+  if ((st = check_ptr(k_out)) != SKV_OK) return st;
+  if ((st = check_ptr(v_out)) != SKV_OK) return st;
+  const skv::Geometry& g = c->g;
+  const int n = c->ring.n_cached(g);
+  for (int i = 0; i < n && frame_ids_host; ++i) frame_ids_host[i] = c->ring.cached_frame(g, i);
+  if (n == 0) return SKV_OK;
+  skv::FrameRun runs[3];
+  int nruns = 0;
+  for (int i = 0; i < n; ++i) {
+    const int slot = c->ring.slot_of(g, c->ring.cached_frame(g, i));
+    if (nruns > 0 && runs[nruns - 1].src0 + runs[nruns - 1].count == slot) {
+      ++runs[nruns - 1].count;
+    } else {
+      if (nruns == 3) return SKV_ERR_STATE;  // cannot happen: sinks + at most two ring runs
+      runs[nruns++] = skv::FrameRun{i, 1, slot, i};
+    }
+  }
+  const skv::TokView src[2] = {store_view(g, c->k_store), store_view(g, c->v_store)};
+  const skv::TokView dst[2] = {token_view(g, k_out), token_view(g, v_out)};
+  return launched(c, skv::launch_copy_frames(src, dst, runs, nruns, n, g.F, g.H, g.D, g.elt, (hipStream_t)stream));
+}
+
+}  // extern "C"

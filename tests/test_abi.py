@@ -1,0 +1,112 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skv.h")
+
+skv = pytest.importorskip("streaming_kv_cache_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 13, names
+    lib = ctypes.CDLL(skv._LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in skv.h but not exported"
+    assert set(names) == set(skv.EXPORTED)
+
+
+def test_version_and_strings():
+    assert skv.lib.skv_abi_version() == 1
+    for code in range(7):
+        assert skv.status_string(code)
+    assert skv.status_string(99) == "unknown status"
+
+
+ABOT = skv.Config(24, 128, 22, 40, 3, 5, 21, rope_mode=skv.ROPE_REL)
+LB480 = skv.Config(40, 128, 30, 52, 4, 6, 18)
+
+
+def test_cache_bytes():
+    store, ws = skv.cache_bytes(ABOT)
+    assert store == 21 * 880 * 24 * 128 * 2
+    assert ws == (21 - 3) * 880 * 24 * 128 * 2
+    store, ws = skv.cache_bytes(LB480)
+    assert store == 18 * 1560 * 40 * 128 * 2 and ws == 0
+    tiny = skv.Config(2, 64, 4, 4, 2, 1, 4, dtype=skv.F32)
+    assert skv.cache_bytes(tiny) == (4 * 16 * 2 * 64 * 4, 0)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(heads=0), dict(head_dim=96), dict(head_dim=32), dict(grid_h=0), dict(chunk_frames=0),
+    dict(sink_frames=-1), dict(window_frames=7), dict(rope_split=(40, 40, 40)), dict(rope_split=(43, 43, 42)),
+    dict(rope_theta=-1.0), dict(dtype=7), dict(rope_mode=3),
+])
+def test_bad_configs(bad):
+    base = dict(heads=2, head_dim=128, grid_h=3, grid_w=3, chunk_frames=2, sink_frames=2, window_frames=8)
+    base.update({k: v for k, v in bad.items() if k in base})
+    cfg = skv.Config(**base, **{k: v for k, v in bad.items() if k not in base})
+    if bad == dict(window_frames=7):
+        cfg = skv.Config(2, 128, 3, 3, 4, 4, 7)
+    with pytest.raises(skv.SkvError) as e:
+        skv.cache_bytes(cfg)
+    assert e.value.status == skv.ERR_CONFIG
+
+
+def _init(cfg, k=0x10000, v=0x20000, ws=0x30000):
+    h = ctypes.c_void_p()
+    c = cfg.c_struct()
+    st = skv.lib.kv_cache_init(ctypes.byref(c), ctypes.c_void_p(k), ctypes.c_void_p(v), ctypes.c_void_p(ws),
+                               ctypes.byref(h))
+    return st, h
+
+
+def test_init_validation_and_info():
+    # the handle records pointers only; fake aligned addresses never reach the GPU here
+    assert _init(LB480, k=0)[0] == skv.ERR_NULL
+    assert _init(LB480, k=0x10008)[0] == skv.ERR_ALIGN
+    assert _init(ABOT, ws=0)[0] == skv.ERR_NULL
+    st, h = _init(ABOT)
+    assert st == skv.OK
+    info = skv.KvCacheInfo()
+    assert skv.lib.kv_cache_info(h, ctypes.byref(info)) == skv.OK
+    assert (info.n_appended, info.n_cached, info.n_vis, info.ring_start, info.poisoned) == (0, 0, 3, -1, 0)
+    nul = ctypes.c_void_p(0)
+    p = ctypes.c_void_p(0x40000)
+    # argument checks that return before anything is enqueued
+    assert skv.lib.kv_cache_append_evict(h, p, p, 0, nul) == skv.ERR_SHAPE
+    assert skv.lib.kv_cache_append_evict(h, p, p, 17, nul) == skv.ERR_SHAPE
+    assert skv.lib.kv_cache_append_evict(h, nul, p, 3, nul) == skv.ERR_NULL
+    assert skv.lib.kv_cache_append_evict(h, ctypes.c_void_p(0x40004), p, 3, nul) == skv.ERR_ALIGN
+    assert skv.lib.rope_apply(h, p, p, 2, 0, nul) == skv.ERR_SHAPE          # rel: n_frames must equal c
+    assert skv.lib.chunk_attention(h, p, p, p, 2, p, nul) == skv.ERR_SHAPE
+    assert skv.lib.chunk_attention(h, p, p, nul, 3, p, nul) == skv.ERR_NULL
+    assert skv.lib.kv_cache_gather(h, nul, p, None, nul) == skv.ERR_NULL
+    assert skv.lib.kv_cache_reset(h) == skv.OK
+    assert skv.lib.kv_cache_destroy(h) == skv.OK
+    assert skv.lib.kv_cache_destroy(nul) == skv.OK
+    st, h = _init(LB480)
+    assert skv.lib.rope_apply_window(h, nul) == skv.ERR_STATE              # abs mode has no window
+    assert skv.lib.rope_apply(h, p, p, 4, -1, nul) == skv.ERR_SHAPE         # abs: start_frame >= 0
+    skv.lib.kv_cache_destroy(h)
+
+
+def test_cross_attention_validation():
+    p, nul = ctypes.c_void_p(0x40000), ctypes.c_void_p(0)
+    f = skv.lib.cross_attention
+    assert f(nul, 8, p, p, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_NULL
+    assert f(p, 8, p, p, 512, 40, 96, skv.BF16, p, nul) == skv.ERR_CONFIG
+    assert f(p, 8, p, p, 0, 40, 128, skv.BF16, p, nul) == skv.ERR_SHAPE
+    assert f(p, 0, p, p, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_SHAPE
+    assert f(p, 8, p, p, 512, 0, 128, skv.BF16, p, nul) == skv.ERR_CONFIG

@@ -1,0 +1,272 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars: cache contents bit-exact; attention within max-abs 2e-2 / mean-abs 2e-3 /
+relative RMS 1e-2 in bf16 and max-abs 1e-5 in fp32; RoPE within one bf16 ulp
+(fp32: 1e-6 of the pair norm) of the fp64 value.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+from oracle import skv_oracle as so
+from tests import rollout as ro
+
+skv = pytest.importorskip("streaming_kv_cache_amd")
+from streaming_kv_cache_amd.workloads import WORKLOADS  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = ["tiny", "small_abs", "small_rel", "small_d64", "small_f32_rel", "small_nosink"]
+
+
+# ------------------------------------------------------------------ cache update
+@pytest.mark.parametrize("name", SMALL)
+def test_append_gather_bitexact(name):
+    wl = WORKLOADS[name]
+    c = wl.cfg
+    say(f"[append/gather] {name}")
+    cache = skv.KVCache(c)
+    cl = so.CacheList(c.sink_frames, c.window_frames)
+    rng = np.random.default_rng(1)
+    for step in range(40):
+        n = c.chunk_frames if rng.random() < 0.6 else int(rng.integers(1, c.window_frames - c.sink_frames + 1))
+        k = ro.draw(wl, n, step, 0, si.K)
+        v = ro.draw(wl, n, step, 0, si.V)
+        cache.append_evict(k.cuda(), v.cuda())
+        f = c.tokens_per_frame
+        cl.append([k[i * f:(i + 1) * f] for i in range(n)], [v[i * f:(i + 1) * f] for i in range(n)])
+        gk, gv, ids = cache.gather()
+        torch.cuda.synchronize()
+        assert ids == cl.frame_ids()
+        ek = torch.cat([e[1] for e in cl.entries])
+        ev = torch.cat([e[2] for e in cl.entries])
+        assert torch.equal(gk.cpu(), ek) and torch.equal(gv.cpu(), ev), f"step {step}"
+
+
+def test_sinks_survive_300_chunks():
+    wl = WORKLOADS["small_abs"]
+    c = wl.cfg
+    say("[sinks] small_abs 300 chunks")
+    cache = skv.KVCache(c)
+    f = c.tokens_per_frame
+    first = []
+    for ch in range(300):
+        k = ro.draw(wl, c.chunk_frames, ch, 0, si.K).cuda()
+        v = ro.draw(wl, c.chunk_frames, ch, 0, si.V).cuda()
+        cache.append_evict(k, v)
+        if ch == 0:
+            first = [k.clone(), v.clone()]
+    gk, gv, ids = cache.gather()
+    torch.cuda.synchronize()
+    s = c.sink_frames
+    assert ids[:s] == list(range(s)) and ids[-1] == 300 * c.chunk_frames - 1
+    assert torch.equal(gk[:s * f], first[0][:s * f]) and torch.equal(gv[:s * f], first[1][:s * f])
+
+
+# ------------------------------------------------------------------ RoPE
+def _rope_close(got, ref, dtype):
+    g = got.float().cpu().double().numpy()
+    if dtype == skv.F32:
+        pair = np.abs(ref[..., 0::2]) + np.abs(ref[..., 1::2])
+        bound = 1e-6 * np.repeat(pair, 2, axis=-1) + 1e-30
+        assert np.all(np.abs(g - ref) <= bound)
+    else:
+        # one bf16 ulp of the exact value, plus the fp32 rounding of the rotation itself
+        a = np.abs(ref)
+        ulp = np.where(a > 0, 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7), 2.0 ** -133)
+        pair = np.repeat(np.abs(ref[..., 0::2]) + np.abs(ref[..., 1::2]), 2, axis=-1)
+        bound = ulp + 2.0 ** -20 * pair
+        assert np.all(np.abs(g - ref) <= bound), float(np.max(np.abs(g - ref) / bound))
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_abs", "small_d64", "lb480"])
+@pytest.mark.parametrize("start", [0, 7, 1199])
+def test_rope_abs(name, start):
+    wl = WORKLOADS[name]
+    c = wl.cfg
+    say(f"[rope abs] {name} start={start}")
+    cache = skv.KVCache(c)
+    x = ro.draw(wl, c.chunk_frames, start, 0, si.Q)
+    got = cache.rope_apply(x.cuda(), start_frame=start)
+    torch.cuda.synchronize()
+    orc = ro.oracle_for(wl)
+    ref = so.rope_3d(ro.f64(x), range(start, start + c.chunk_frames), c.grid_h, c.grid_w, orc.split)
+    _rope_close(got, ref, c.dtype)
+    # in place
+    xd = x.cuda()
+    cache.rope_apply(xd, out=xd, start_frame=start)
+    torch.cuda.synchronize()
+    assert torch.equal(xd, got)
+
+
+@pytest.mark.parametrize("name", ["small_rel", "small_f32_rel", "abot720"])
+def test_rope_rel_and_window(name):
+    wl = WORKLOADS[name]
+    c = wl.cfg
+    say(f"[rope rel] {name}")
+    cache = skv.KVCache(c)
+    orc = ro.oracle_for(wl)
+    ro.prefill(wl, cache, orc)
+    f = c.tokens_per_frame
+    for ch in range(wl.steady_chunk + 3):
+        x = ro.draw(wl, c.chunk_frames, ch, 1, si.Q)
+        got = cache.rope_apply(x.cuda())
+        cache.rope_apply_window()
+        torch.cuda.synchronize()
+        ref = orc._rope(ro.f64(x), orc.query_time_ids())
+        _rope_close(got, ref, c.dtype)
+        # window: visible history k_raw rotated at slot ids, logical order, head-major workspace
+        hist = orc.visible()
+        if hist and (ch % 2 == 0 or ch == wl.steady_chunk + 2):
+            nh = len(hist)
+            ws = cache.workspace.view(c.torch_dtype).view(c.heads, (c.window_frames - c.chunk_frames) * f,
+                                                          c.head_dim)[:, :nh * f]
+            wsd = ws.permute(1, 0, 2).contiguous()
+            refw = np.concatenate([orc._rope(e[1], [j]) for j, e in enumerate(hist)])
+            _rope_close(wsd, refw, c.dtype)
+        k = ro.draw(wl, c.chunk_frames, ch, 4, si.K)
+        v = ro.draw(wl, c.chunk_frames, ch, 4, si.V)
+        cache.append_evict(k.cuda(), v.cuda())
+        orc.append(ro.f64(k), ro.f64(v))
+
+
+# ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("name", SMALL)
+def test_rollout_parity(name):
+    wl = WORKLOADS[name]
+    say(f"[rollout] {name} chunks={wl.n_chunks}")
+    worst = (0.0, 0.0, 0.0)
+    for ch, p, out, ref in ro.rollout(wl, wl.n_chunks):
+        torch.cuda.synchronize()
+        e = ro.assert_close(out, ref, wl.cfg.dtype, f"{name} chunk {ch} pass {p}")
+        worst = tuple(max(a, b) for a, b in zip(worst, e))
+    say(f"  worst max/mean/relrms = {worst}")
+
+
+def _probe_rollout(wl, mode):
+    """q = 0 with one-hot (mode 'onehot') or random (mode 'zeroq') values: the answer is a plain mean."""
+    c = wl.cfg
+    f = c.tokens_per_frame
+    cache = skv.KVCache(c)
+    orc = ro.oracle_for(wl)
+    ro.prefill(wl, cache, orc)
+    lq = c.chunk_frames * f
+
+    def values(first_frame, n, ch):
+        if mode == "zeroq":
+            return ro.draw(wl, n, ch, 2, si.V)
+        v = torch.zeros(n * f, c.heads, c.head_dim)
+        for i in range(n):
+            v[i * f:(i + 1) * f, :, (first_frame + i) % c.head_dim] = 1.0
+        return v.to(c.torch_dtype)
+
+    if wl.prefill:  # replace the random sink values by probe values (same frames)
+        cache.reset()
+        orc = ro.oracle_for(wl)
+        sk = ro.draw(wl, wl.prefill, 0, 0, si.SINK_K)
+        sv = values(0, wl.prefill, 0)
+        cache.append_evict(sk.cuda(), sv.cuda())
+        orc.append(ro.f64(sk), ro.f64(sv))
+    for ch in range(wl.n_chunks):
+        t = cache.info().n_appended
+        if c.rope_mode == skv.ROPE_REL:
+            cache.rope_apply_window()
+        q = torch.zeros(lq, c.heads, c.head_dim, dtype=c.torch_dtype)
+        k = ro.draw(wl, c.chunk_frames, ch, 1, si.K)
+        v = values(t, c.chunk_frames, ch)
+        out, k_app, v_app = ro.gpu_pass(cache, q, k, v)
+        torch.cuda.synchronize()
+        ref = orc.chunk_attention(ro.f64(q), ro.f64(k), ro.f64(v))
+        g = out.float().cpu().double().numpy()
+        if mode == "onehot":
+            # exact closed form: 1/n_vis on each visible frame's channel
+            vis = [e[0] for e in orc.visible()] + list(range(t, t + c.chunk_frames))
+            expect = np.zeros(c.head_dim)
+            for fr in vis:
+                expect[fr % c.head_dim] += 1.0 / len(vis)
+            assert np.allclose(ref, expect[None, None], atol=1e-12)
+            tol = 1e-5 if c.dtype == skv.F32 else 2.0 ** -8 * expect.max() + 1e-6
+            assert np.abs(g - expect[None, None]).max() <= tol, f"chunk {ch}"
+        else:
+            ro.assert_close(out, ref, c.dtype, f"zero-q chunk {ch}")
+        cache.append_evict(k_app, v_app)
+        orc.append(ro.f64(k), ro.f64(v))
+
+
+@pytest.mark.parametrize("name", ["small_abs", "small_rel", "tiny", "small_nosink"])
+@pytest.mark.parametrize("mode", ["onehot", "zeroq"])
+def test_visibility_probes(name, mode):
+    say(f"[probe] {name} {mode}")
+    _probe_rollout(WORKLOADS[name], mode)
+
+
+@pytest.mark.parametrize("dtype,n_q,n_text,h,d", [
+    (skv.BF16, 1000, 512, 5, 128), (skv.BF16, 130, 77, 3, 64), (skv.F32, 70, 512, 2, 128), (skv.F32, 33, 9, 1, 32),
+])
+def test_cross_attention(dtype, n_q, n_text, h, d):
+    say(f"[cross] dtype={dtype} n_q={n_q} n_text={n_text} h={h} d={d}")
+    tdt = torch.bfloat16 if dtype == skv.BF16 else torch.float32
+    q = si.draw((n_q, h, d), 0, 0, 0, si.Q, tdt)
+    kt = si.draw((n_text, h, d), 0, 0, 0, si.TEXT_K, tdt)
+    vt = si.draw((n_text, h, d), 0, 0, 0, si.TEXT_V, tdt)
+    out = skv.cross_attention(q.cuda(), kt.cuda(), vt.cuda())
+    torch.cuda.synchronize()
+    ref = so.cross_attention(ro.f64(q), ro.f64(kt), ro.f64(vt))
+    ro.assert_close(out, ref, dtype, "cross")
+
+
+def test_determinism():
+    say("[determinism] small_rel twice")
+    wl = WORKLOADS["small_rel"]
+    a = [o.clone() for _, _, o, _ in ro.rollout(wl, 6, with_oracle=False)]
+    b = [o.clone() for _, _, o, _ in ro.rollout(wl, 6, with_oracle=False)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_edge_window_equals_sink_plus_chunk():
+    """W = S + c: a chunk sees only the sinks and itself."""
+    say("[edge] W = S + c")
+    cfg = skv.Config(2, 128, 3, 7, 2, 1, 3, skv.ROPE_ABS, skv.BF16)
+    from streaming_kv_cache_amd.workloads import Workload
+    wl = Workload("edge", cfg, n_chunks=6)
+    for ch, p, out, ref in ro.rollout(wl, 6, passes=(0, ro.WRITE_BACK)):
+        torch.cuda.synchronize()
+        ro.assert_close(out, ref, cfg.dtype, f"edge chunk {ch}")
+
+
+# ------------------------------------------------------------------ full-size shapes
+def _rows(lq, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    r = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, lq - 1], rng.integers(0, lq, n)]))
+    return r[r < lq]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["abot720", "lb480", "lb720"])
+def test_full_size_sampled(name):
+    """Roll out to the first steady chunk and one past it; compare sampled query rows (all heads)."""
+    wl = WORKLOADS[name]
+    rows = _rows(wl.lq)
+    last = wl.steady_chunk + 1
+    say(f"[full] {name} to chunk {last}, {len(rows)} rows")
+    checked = 0
+    for ch, p, out, ref in ro.rollout(wl, last + 1, passes=(0, ro.WRITE_BACK), rows=rows,
+                                      oracle_chunks={0, wl.steady_chunk, last}):
+        if ref is None:
+            continue
+        torch.cuda.synchronize()
+        got = out[torch.as_tensor(rows, device=out.device)]
+        e = ro.assert_close(got, ref, wl.cfg.dtype, f"{name} chunk {ch} pass {p}")
+        say(f"  chunk {ch} pass {p}: max {e[0]:.3g} mean {e[1]:.3g} relrms {e[2]:.3g}")
+        checked += 1
+    assert checked == 6
