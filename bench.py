@@ -1,0 +1,277 @@
+"""Benchmark of the streaming KV-cache hot path on one MI355X.
+
+A step is one generated chunk in steady state (the cache window is full):
+  [REL] rope_apply_window once, then 4 denoise passes + 1 clean write-back pass,
+  each pass = rope(q), rope(k), chunk_attention (+ cross_attention when the
+  workload has text tokens), and after the write-back pass kv_cache_append_evict.
+Inputs are seeded N(0,1) tensors already resident in HBM when timing starts.
+
+Prints ONE JSON line.  `value` is whole-step attention throughput: the
+attention FLOPs of a step (4 * Lq * Lkv * D * H per pass, visible pairs only)
+over the measured wall time per step.  `roofline` reports the attention kernel
+alone (its average duration from HIP events on the launch stream).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="abot720")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--pool", type=int, default=2, help="device-resident input sets cycled over steps")
+    return ap.parse_args()
+
+
+def kernel_sha(name: str) -> str:
+    p = os.path.join(ROOT, "streaming_kv_cache_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+class Runner:
+    def __init__(self, wl, pool_sets: int):
+        import torch
+        import seeded_inputs as si
+        import streaming_kv_cache_amd as skv
+        self.torch, self.si, self.skv = torch, si, skv
+        self.wl = wl
+        cfg = wl.cfg
+        self.cfg = cfg
+        self.rel = cfg.rope_mode == skv.ROPE_REL
+        self.caches = [skv.KVCache(cfg) for _ in range(wl.layers)]
+        c, f, h, d = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim
+        shape = (c * f, h, d)
+        dt = cfg.torch_dtype
+        # input pool: pool_sets x 5 passes x (q, k, v), drawn with the seed recipe, then moved to HBM
+        self.cpu_pool = []
+        self.pool = []
+        for sidx in range(pool_sets):
+            passes_cpu, passes_dev = [], []
+            for p in range(wl.passes):
+                qkv = [si.draw(shape, 0, sidx, p, tid, dt) for tid in (si.Q, si.K, si.V)]
+                passes_cpu.append(qkv)
+                passes_dev.append([x.cuda() for x in qkv])
+            self.cpu_pool.append(passes_cpu)
+            self.pool.append(passes_dev)
+        if wl.text_tokens:
+            tshape = (wl.text_tokens, h, d)
+            self.text = [si.draw(tshape, 0, 0, 0, si.TEXT_K, dt).cuda(), si.draw(tshape, 0, 0, 0, si.TEXT_V, dt).cuda()]
+            self.xout = torch.empty(shape, dtype=dt, device="cuda")
+        self.qr = torch.empty(shape, dtype=dt, device="cuda")
+        self.kr = [torch.empty(shape, dtype=dt, device="cuda") for _ in range(wl.layers)]
+        self.out = torch.empty(shape, dtype=dt, device="cuda")
+        self.chunk = 0
+        self.ev = None
+
+    def prefill(self):
+        si, wl, cfg = self.si, self.wl, self.cfg
+        if not wl.prefill:
+            return
+        shape = (wl.prefill * cfg.tokens_per_frame, cfg.heads, cfg.head_dim)
+        sk = si.draw(shape, 0, 0, 0, si.SINK_K, cfg.torch_dtype).cuda()
+        sv = si.draw(shape, 0, 0, 0, si.SINK_V, cfg.torch_dtype).cuda()
+        for cache in self.caches:
+            k = sk if self.rel else cache.rope_apply(sk, start_frame=0)
+            cache.append_evict(k, sv)
+
+    def _ev(self, kind):
+        if self.ev is None:
+            return
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.ev[kind].append(e)
+
+    def step(self):
+        wl = self.wl
+        sets = self.pool[self.chunk % len(self.pool)]
+        self._ev("step0")
+        if self.rel:
+            self._ev("win0")
+            for cache in self.caches:
+                cache.rope_apply_window()
+            self._ev("win1")
+        for p in range(wl.passes):
+            q, k, v = sets[p]
+            for li, cache in enumerate(self.caches):
+                t = cache.info().n_appended
+                self._ev("rope0")
+                cache.rope_apply(q, out=self.qr, start_frame=t)
+                cache.rope_apply(k, out=self.kr[li], start_frame=t)
+                self._ev("rope1")
+                self._ev("attn0")
+                cache.chunk_attention(self.qr, self.kr[li], v, out=self.out)
+                self._ev("attn1")
+                if wl.text_tokens:
+                    self._ev("cross0")
+                    self.skv.cross_attention(q, self.text[0], self.text[1], out=self.xout)
+                    self._ev("cross1")
+                if p == wl.passes - 1:
+                    self._ev("app0")
+                    cache.append_evict(k if self.rel else self.kr[li], v)
+                    self._ev("app1")
+        self._ev("step1")
+        self.chunk += 1
+
+    def visible(self):
+        return self.caches[0].info().n_vis
+
+
+def avg_ms(ev, a, b):
+    xs = [s.elapsed_time(e) for s, e in zip(ev[a], ev[b])]
+    return (float(np.mean(xs)) if xs else 0.0), xs
+
+
+def cpu_baseline(runner, target_s):
+    """Time the oracle (as it stands) on a bounded sample of one steady pass: a subset of query rows."""
+    import seeded_inputs as si
+    from oracle import skv_oracle as so
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    wl, cfg = runner.wl, runner.cfg
+    orc = so.StreamingOracle(cfg.heads, cfg.head_dim, cfg.grid_h, cfg.grid_w, cfg.chunk_frames, cfg.sink_frames,
+                             cfg.window_frames, rope_mode="rel" if runner.rel else "abs")
+    f = cfg.tokens_per_frame
+    if wl.prefill:
+        shape = (wl.prefill * f, cfg.heads, cfg.head_dim)
+        orc.append(si.to_f64(si.draw(shape, 0, 0, 0, si.SINK_K, cfg.torch_dtype)),
+                   si.to_f64(si.draw(shape, 0, 0, 0, si.SINK_V, cfg.torch_dtype)))
+    sets = runner.cpu_pool
+    ch = 0
+    while orc.n_vis() < cfg.window_frames:
+        _, k, v = sets[ch % len(sets)][wl.passes - 1]
+        orc.append(si.to_f64(k), si.to_f64(v))
+        ch += 1
+    q, k, v = [si.to_f64(x) for x in sets[0][0]]
+    lq, lkv = q.shape[0], orc.n_vis() * f
+    rows = np.arange(0, lq, max(1, lq // 64))[:64]
+    t0 = time.perf_counter()
+    orc.chunk_attention(q, k, v, rows=rows)
+    dt = time.perf_counter() - t0
+    n = int(min(lq, max(len(rows), len(rows) * target_s / max(dt, 1e-3))))
+    rows = np.linspace(0, lq - 1, n).astype(np.int64)
+    t0 = time.perf_counter()
+    orc.chunk_attention(q, k, v, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * len(rows) * lkv * cfg.head_dim * cfg.heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one steady {wl.name} pass (Lkv={lkv}), {len(rows)} of {lq} query rows x {cfg.heads} heads, "
+                      f"fp64 NumPy incl. RoPE of the visible keys; {dt:.1f} s"}
+
+
+def traffic_from_profile(wl_name, per_launch_algo_bytes):
+    """HBM bytes per attention launch from committed rocprofv3 counters, if taken on the current kernel."""
+    p = os.path.join(ROOT, "profiles", f"attn_bf16_{wl_name}_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_sha") != kernel_sha("attn_bf16.hip"):
+        return None
+    return d.get("hbm_bytes_per_dispatch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build targets one GPU: run with --gpus 1 (no multi-GPU path)"}))
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    import torch
+    from streaming_kv_cache_amd.workloads import WORKLOADS
+    import streaming_kv_cache_amd as skv
+    wl = WORKLOADS[args.workload]
+    cfg = wl.cfg
+    torch.cuda.set_device(0)
+    r = Runner(wl, max(1, args.pool))
+    r.prefill()
+    while r.visible() < cfg.window_frames:   # fill the window (not timed)
+        r.step()
+    for _ in range(args.warmup):
+        r.step()
+    torch.cuda.synchronize()
+    r.ev = {k: [] for k in ("step0", "step1", "win0", "win1", "rope0", "rope1", "attn0", "attn1", "cross0",
+                            "cross1", "app0", "app1")}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        r.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = r.ev
+    ms_step = wall * 1e3 / args.steps
+    attn_ms, _ = avg_ms(ev, "attn0", "attn1")
+    app_ms, _ = avg_ms(ev, "app0", "app1")
+    rope_ms, _ = avg_ms(ev, "rope0", "rope1")
+    win_ms, _ = avg_ms(ev, "win0", "win1")
+    cross_ms, _ = avg_ms(ev, "cross0", "cross1")
+    _, steps_ms = avg_ms(ev, "step0", "step1")
+
+    c, f, h, d = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim
+    elt = 2 if cfg.dtype == skv.BF16 else 4
+    lq, lkv = c * f, cfg.window_frames * f
+    attn_flop = 4.0 * lq * lkv * d * h                       # per pass per layer
+    step_flop = attn_flop * wl.passes * wl.layers
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    app_bytes = 2 * 2 * lq * h * d * elt                      # K and V, read + write
+    rope_bytes = 2 * 2 * lq * h * d * elt                     # q and k, read + write
+    bf16 = cfg.dtype == skv.BF16
+    peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_VECTOR_PEAK_TFLOPS
+    roof = {"bound": "mfma" if bf16 else "alu", "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(attn_tflops / peak, 4),
+            "traffic": traffic_from_profile(wl.name, None), "kernel": "attn_bf16_kernel" if bf16 else "attn_f32_kernel",
+            "avg_kernel_ms": round(attn_ms, 4), "algorithmic_flop_per_launch": attn_flop}
+    out = {
+        "metric": "chunk-attention TFLOP/s + % bf16 MFMA peak; cache-update GB/s; per-chunk ms",
+        "value": round(step_flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic: seeded N(0,1) q/k/v (torch CPU generator, RNE to bf16), device-resident",
+        "config": {"workload": wl.name, "heads": h, "head_dim": d, "tokens_per_frame": f, "chunk_frames": c,
+                   "sink_frames": cfg.sink_frames, "window_frames": cfg.window_frames, "lq": lq, "lkv": lkv,
+                   "rope": "relative" if r.rel else "absolute", "layers": wl.layers, "passes_per_chunk": wl.passes,
+                   "text_tokens": wl.text_tokens},
+        "roofline": roof,
+        "chunk_attention": {"tflops": round(attn_tflops, 2), "frac_peak": round(attn_tflops / peak, 4),
+                            "avg_ms": round(attn_ms, 4)},
+        "cache_update": {"GB/s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(app_bytes / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "avg_us": round(app_ms * 1e3, 2), "bytes": app_bytes},
+        "rope_qk": {"GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1), "avg_us": round(rope_ms * 1e3, 2)},
+        "per_chunk_ms": {"mean": round(float(np.mean(steps_ms)), 4), "p50": round(float(np.median(steps_ms)), 4),
+                         "p99": round(float(np.percentile(steps_ms, 99)), 4)},
+    }
+    if r.rel:
+        win_bytes = 2 * (cfg.window_frames - c) * f * h * d * elt
+        out["rope_window"] = {"GB/s": round(win_bytes / (win_ms * 1e-3) / 1e9, 1), "avg_us": round(win_ms * 1e3, 2)}
+    if wl.text_tokens:
+        xf = 4.0 * lq * wl.text_tokens * d * h
+        out["cross_attention"] = {"tflops": round(xf / (cross_ms * 1e-3) / 1e12, 2), "avg_ms": round(cross_ms, 4)}
+    if not args.no_cpu_baseline and wl.layers == 1:
+        out["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,6 +4,8 @@
 // reduced-precision matrix instructions): one wave per (head, 64 queries), one
 // query row per lane, K/V tiles of 64 keys staged in LDS and read as
 // broadcasts.  Online softmax over chunks of 16 keys (max, rescale, exp2).
+// V is read through general strides, so the transposed V store and token-major
+// V (cross attention) share the kernel.
 #include "skv_device.hpp"
 #include "skv_kernels.hpp"
 
@@ -43,7 +45,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
         if (key < nk) {
           kv = *(const f32x4_t*)(kb + (int64_t)(off + key) * sg.k_rs + c);
-          vv = *(const f32x4_t*)(vb + (int64_t)(off + key) * sg.v_rs + c);
+          const float* vr = vb + (int64_t)(off + key) * sg.v_rs;
+          if (sg.v_ds == 1) {
+            vv = *(const f32x4_t*)(vr + c);
+          } else {  // transposed V
+            vv = f32x4_t{vr[c * sg.v_ds], vr[(c + 1) * sg.v_ds], vr[(c + 2) * sg.v_ds], vr[(c + 3) * sg.v_ds]};
+          }
         }
         *(f32x4_t*)&Ks[key][c] = kv;
         *(f32x4_t*)&Vs[key][c] = vv;

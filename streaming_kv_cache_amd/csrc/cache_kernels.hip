@@ -11,8 +11,8 @@
 namespace skv {
 
 // ---------------------------------------------------------------- frame copy
-// Copies whole frames between two token views, for K and V at once
-// (blockIdx.y selects the tensor).  Used by
+// Copies whole frames between two token views, for up to two tensors at once
+// (blockIdx.y selects the tensor).  Used for the keys by
 //   * kv_cache_append_evict: caller's token-major chunk -> ring slots of the
 //     head-major stores ([LB-fast] 3. KV 缓存 滚动窗口: write the clean chunk;
 //     the ring slot of a frame is the one its evicted predecessor held), and
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_frames_kernel(CopyArgs a) {
   }
 }
 
-hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], const FrameRun* runs, int nruns,
-                              int n_frames, int F, int H, int D, int elt, hipStream_t stream) {
+hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], int n_tensors, const FrameRun* runs,
+                              int nruns, int n_frames, int F, int H, int D, int elt, hipStream_t stream) {
   CopyArgs a;
   for (int i = 0; i < 2; ++i) {
     a.src[i] = src[i];
@@ -75,7 +75,7 @@ hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], const 
   a.row_vec_shift = sh;
   a.elt = elt;
   a.n_tok = n_frames * F;
-  dim3 grid((a.n_tok + kCopyTokPerBlock - 1) / kCopyTokPerBlock, 2);
+  dim3 grid((a.n_tok + kCopyTokPerBlock - 1) / kCopyTokPerBlock, n_tensors);
   hipLaunchKernelGGL(copy_frames_kernel, grid, dim3(kCopyThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -40,12 +40,15 @@ struct TokView {
 };
 
 // One contiguous range of visible keys for the attention kernels.
-// key j of the range, head h: K at k + j*k_rs + h*k_hs, V at v + j*v_rs + h*v_hs.
+// Key j of the range, head h, dim d: K at k + j*k_rs + h*k_hs + d,
+// V at v + h*v_hs + j*v_rs + d*v_ds (token-major V: v_rs = H*D, v_ds = 1;
+// transposed V: v_rs = 1, v_ds = row length).
 struct KvSeg {
   const void* k;
   const void* v;
-  int64_t k_hs, k_rs, v_hs, v_rs;
-  int32_t n, pad_;
+  int64_t k_hs, k_rs, v_hs, v_rs, v_ds;
+  int32_t n;
+  int32_t v_al16;  // transposed V: row starts and the range start are 16-byte aligned
 };
 
 struct AttnArgs {

@@ -7,9 +7,26 @@
 
 namespace skv {
 
-// Copy n_frames whole frames of K (index 0) and V (index 1) from src to dst views.
-hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], const FrameRun* runs, int nruns,
-                              int n_frames, int F, int H, int D, int elt, hipStream_t stream);
+// Copy n_frames whole frames of n_tensors (1 or 2) token views from src to dst.
+hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], int n_tensors, const FrameRun* runs,
+                              int nruns, int n_frames, int F, int H, int D, int elt, hipStream_t stream);
+
+// Token-major <-> transposed V (V^T[h][d][key]).  runs map launch frames to
+// frame positions in V^T key space (dst0); nruns == 0 means key = token and a
+// zero-filled row tail up to row_pad keys (tok_to_vt only).
+struct VtCopyArgs {
+  void* tok_base;
+  int64_t tok_stride, head_stride;
+  void* vt_base;
+  int64_t vt_hs, vt_ds;
+  FrameRun runs[3];
+  int32_t nruns;
+  int32_t F, H, D;
+  int32_t n_tok;
+  int32_t row_pad;
+};
+hipError_t launch_tok_to_vt(const VtCopyArgs& a, int elt, hipStream_t stream);
+hipError_t launch_vt_to_tok(const VtCopyArgs& a, int elt, hipStream_t stream);
 
 struct RopeLaunch {
   TokView src, dst;
@@ -25,7 +42,9 @@ struct RopeLaunch {
 hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream);
 
 // softmax(q K^T * scale) V over the concatenated key ranges of a.seg.
-hipError_t launch_attention_bf16(const AttnArgs& a, int D, hipStream_t stream);
+// bf16, V transposed (cache path) / V token-major (cross attention); fp32 takes any V strides.
+hipError_t launch_attention_bf16_vt(const AttnArgs& a, int D, hipStream_t stream);
+hipError_t launch_attention_bf16_tokv(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, int D, hipStream_t stream);
 
 }  // namespace skv

@@ -55,6 +55,15 @@ skv::TokView token_view(const skv::Geometry& g, const void* base) {
 
 float softmax_scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
 
+// V store: V^T[h][d][key], key = slot*F + token, rows of W*F keys.
+int64_t vt_row(const skv::Geometry& g) { return (int64_t)g.W * g.F; }
+// Current-chunk V^T rows in the workspace: c*F keys padded to a multiple of 64.
+int64_t cur_row(const skv::Geometry& g) { return ((int64_t)g.c * g.F + 63) / 64 * 64; }
+// Workspace: [REL window keys, (W-c)*F*H*D] then [current-chunk V^T, H*D*cur_row].
+int64_t ws_window_elems(const skv::Geometry& g) { return skv::workspace_elems(g); }
+int64_t ws_total_elems(const skv::Geometry& g) { return ws_window_elems(g) + (int64_t)g.H * g.D * cur_row(g); }
+void* ws_vt(const skv_cache* c) { return (char*)c->ws + ws_window_elems(c->g) * c->g.elt; }
+
 }  // namespace
 
 extern "C" {
@@ -80,7 +89,7 @@ skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_
   skv_status st = skv::make_geometry(cfg, &g);
   if (st != SKV_OK) return st;
   *store_bytes_each = (size_t)skv::store_elems(g) * g.elt;
-  *workspace_bytes = (size_t)skv::workspace_elems(g) * g.elt;
+  *workspace_bytes = (size_t)ws_total_elems(g) * g.elt;
   return SKV_OK;
 }
 
@@ -91,13 +100,13 @@ skv_status kv_cache_init(const skv_config* cfg, void* k_store, void* v_store, vo
   if (st != SKV_OK) return st;
   if ((st = check_ptr(k_store)) != SKV_OK) return st;
   if ((st = check_ptr(v_store)) != SKV_OK) return st;
-  if (g.mode == SKV_ROPE_REL && (st = check_ptr(workspace)) != SKV_OK) return st;
+  if ((st = check_ptr(workspace)) != SKV_OK) return st;
   skv_cache* c = new (std::nothrow) skv_cache();
   if (!c) return SKV_ERR_STATE;
   c->g = g;
   c->k_store = k_store;
   c->v_store = v_store;
-  c->ws = g.mode == SKV_ROPE_REL ? workspace : nullptr;
+  c->ws = workspace;
   *out = c;
   return SKV_OK;
 }
@@ -148,10 +157,26 @@ skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int
       runs[nruns++] = skv::FrameRun{i, 1, i, slot};
     }
   }
-  const skv::TokView src[2] = {token_view(g, k), token_view(g, v)};
-  const skv::TokView dst[2] = {store_view(g, c->k_store), store_view(g, c->v_store)};
-  st = launched(c, skv::launch_copy_frames(src, dst, runs, nruns, n_frames, g.F, g.H, g.D, g.elt,
+  const skv::TokView src[2] = {token_view(g, k), token_view(g, k)};
+  const skv::TokView dst[2] = {store_view(g, c->k_store), store_view(g, c->k_store)};
+  st = launched(c, skv::launch_copy_frames(src, dst, 1, runs, nruns, n_frames, g.F, g.H, g.D, g.elt,
                                             (hipStream_t)stream));
+  if (st != SKV_OK) return st;
+  skv::VtCopyArgs va;
+  va.tok_base = const_cast<void*>(v);
+  va.tok_stride = (int64_t)g.H * g.D;
+  va.head_stride = g.D;
+  va.vt_base = c->v_store;
+  va.vt_hs = (int64_t)g.D * vt_row(g);
+  va.vt_ds = vt_row(g);
+  for (int i = 0; i < 3; ++i) va.runs[i] = i < nruns ? runs[i] : skv::FrameRun{0, 0, 0, 0};
+  va.nruns = nruns;
+  va.F = g.F;
+  va.H = g.H;
+  va.D = g.D;
+  va.n_tok = n_frames * g.F;
+  va.row_pad = 0;
+  st = launched(c, skv::launch_tok_to_vt(va, g.elt, (hipStream_t)stream));
   if (st != SKV_OK) return st;
   c->ring.T += n_frames;
   c->window_ready = false;
@@ -242,6 +267,24 @@ skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur
   const bool rel = g.mode == SKV_ROPE_REL;
   if (rel && p.n_hist > 0 && !c->window_ready) return SKV_ERR_STATE;
 
+  // current chunk's V -> V^T rows in the workspace (tail zero-filled to a multiple of 64 keys)
+  skv::VtCopyArgs va;
+  va.tok_base = const_cast<void*>(v_cur);
+  va.tok_stride = (int64_t)g.H * g.D;
+  va.head_stride = g.D;
+  va.vt_base = ws_vt(c);
+  va.vt_hs = (int64_t)g.D * cur_row(g);
+  va.vt_ds = cur_row(g);
+  for (int i = 0; i < 3; ++i) va.runs[i] = skv::FrameRun{0, 0, 0, 0};
+  va.nruns = 0;
+  va.F = g.F;
+  va.H = g.H;
+  va.D = g.D;
+  va.n_tok = g.c * g.F;
+  va.row_pad = (int32_t)cur_row(g);
+  st = launched(c, skv::launch_tok_to_vt(va, g.elt, (hipStream_t)stream));
+  if (st != SKV_OK) return st;
+
   skv::AttnArgs a;
   a.q = q;
   a.out = out;
@@ -251,37 +294,40 @@ skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur
   a.nseg = 0;
   const int64_t store_hs = (int64_t)g.W * g.F * g.D;
   const int64_t ws_hs = (int64_t)(g.W - g.c) * g.F * g.D;
+  const int per16 = 16 / g.elt;
   for (int i = 0; i < p.n_runs; ++i) {
     const skv::SlotRun& r = p.runs[i];
     skv::KvSeg sg;
-    const int64_t slot_off = (int64_t)r.slot0 * g.F * g.D;
     if (rel) {
       sg.k = byte_ptr(c->ws, (int64_t)r.logical0 * g.F * g.D, g.elt);
       sg.k_hs = ws_hs;
     } else {
-      sg.k = byte_ptr(c->k_store, slot_off, g.elt);
+      sg.k = byte_ptr(c->k_store, (int64_t)r.slot0 * g.F * g.D, g.elt);
       sg.k_hs = store_hs;
     }
     sg.k_rs = g.D;
-    sg.v = byte_ptr(c->v_store, slot_off, g.elt);
-    sg.v_hs = store_hs;
-    sg.v_rs = g.D;
+    const int64_t key0 = (int64_t)r.slot0 * g.F;
+    sg.v = byte_ptr(c->v_store, key0, g.elt);
+    sg.v_hs = (int64_t)g.D * vt_row(g);
+    sg.v_rs = 1;
+    sg.v_ds = vt_row(g);
     sg.n = r.frames * g.F;
-    sg.pad_ = 0;
+    sg.v_al16 = (key0 % per16 == 0 && vt_row(g) % per16 == 0) ? 1 : 0;
     a.seg[a.nseg++] = sg;
   }
   skv::KvSeg cur;
   cur.k = k_cur;
-  cur.v = v_cur;
   cur.k_hs = g.D;
   cur.k_rs = (int64_t)g.H * g.D;
-  cur.v_hs = g.D;
-  cur.v_rs = (int64_t)g.H * g.D;
+  cur.v = ws_vt(c);
+  cur.v_hs = (int64_t)g.D * cur_row(g);
+  cur.v_rs = 1;
+  cur.v_ds = cur_row(g);
   cur.n = g.c * g.F;
-  cur.pad_ = 0;
+  cur.v_al16 = 1;
   a.seg[a.nseg++] = cur;
-  for (int i = a.nseg; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0};
-  const hipError_t e = g.dtype == SKV_BF16 ? skv::launch_attention_bf16(a, g.D, (hipStream_t)stream)
+  for (int i = a.nseg; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  const hipError_t e = g.dtype == SKV_BF16 ? skv::launch_attention_bf16_vt(a, g.D, (hipStream_t)stream)
                                             : skv::launch_attention_f32(a, g.D, (hipStream_t)stream);
   return launched(c, e);
 }
@@ -306,9 +352,9 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
   a.sl2 = softmax_scale_log2(head_dim);
   a.nseg = 1;
   a.seg[0] = skv::KvSeg{k_text, v_text, (int64_t)head_dim, (int64_t)heads * head_dim,
-                        (int64_t)head_dim, (int64_t)heads * head_dim, n_text, 0};
-  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0};
-  const hipError_t e = dtype == SKV_BF16 ? skv::launch_attention_bf16(a, head_dim, (hipStream_t)stream)
+                        (int64_t)head_dim, (int64_t)heads * head_dim, 1, n_text, 0};
+  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  const hipError_t e = dtype == SKV_BF16 ? skv::launch_attention_bf16_tokv(a, head_dim, (hipStream_t)stream)
                                          : skv::launch_attention_f32(a, head_dim, (hipStream_t)stream);
   return e == hipSuccess ? SKV_OK : SKV_ERR_HIP;
 }
@@ -334,9 +380,26 @@ skv_status kv_cache_gather(const skv_cache* cc, void* k_out, void* v_out, int64_
       runs[nruns++] = skv::FrameRun{i, 1, slot, i};
     }
   }
-  const skv::TokView src[2] = {store_view(g, c->k_store), store_view(g, c->v_store)};
-  const skv::TokView dst[2] = {token_view(g, k_out), token_view(g, v_out)};
-  return launched(c, skv::launch_copy_frames(src, dst, runs, nruns, n, g.F, g.H, g.D, g.elt, (hipStream_t)stream));
+  const skv::TokView src[2] = {store_view(g, c->k_store), store_view(g, c->k_store)};
+  const skv::TokView dst[2] = {token_view(g, k_out), token_view(g, k_out)};
+  st = launched(c, skv::launch_copy_frames(src, dst, 1, runs, nruns, n, g.F, g.H, g.D, g.elt, (hipStream_t)stream));
+  if (st != SKV_OK) return st;
+  skv::VtCopyArgs va;
+  va.tok_base = v_out;
+  va.tok_stride = (int64_t)g.H * g.D;
+  va.head_stride = g.D;
+  va.vt_base = c->v_store;
+  va.vt_hs = (int64_t)g.D * vt_row(g);
+  va.vt_ds = vt_row(g);
+  for (int i = 0; i < 3; ++i)
+    va.runs[i] = i < nruns ? skv::FrameRun{runs[i].start, runs[i].count, 0, runs[i].src0} : skv::FrameRun{0, 0, 0, 0};
+  va.nruns = nruns;
+  va.F = g.F;
+  va.H = g.H;
+  va.D = g.D;
+  va.n_tok = n * g.F;
+  va.row_pad = 0;
+  return launched(c, skv::launch_vt_to_tok(va, g.elt, (hipStream_t)stream));
 }
 
 }  // extern "C"

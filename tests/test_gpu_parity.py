@@ -128,8 +128,9 @@ def test_rope_rel_and_window(name):
         hist = orc.visible()
         if hist and (ch % 2 == 0 or ch == wl.steady_chunk + 2):
             nh = len(hist)
-            ws = cache.workspace.view(c.torch_dtype).view(c.heads, (c.window_frames - c.chunk_frames) * f,
-                                                          c.head_dim)[:, :nh * f]
+            nwin = c.heads * (c.window_frames - c.chunk_frames) * f * c.head_dim
+            ws = cache.workspace.view(c.torch_dtype)[:nwin].view(c.heads, (c.window_frames - c.chunk_frames) * f,
+                                                                 c.head_dim)[:, :nh * f]
             wsd = ws.permute(1, 0, 2).contiguous()
             refw = np.concatenate([orc._rope(e[1], [j]) for j, e in enumerate(hist)])
             _rope_close(wsd, refw, c.dtype)
