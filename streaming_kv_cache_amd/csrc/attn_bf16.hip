@@ -340,19 +340,25 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void*
 
 }  // namespace
 
+// Cross-half (lanes l and l^32) reductions.
+__device__ __forceinline__ float half_swap_max(float x) { return fmaxf(x, xor32(x)); }
+__device__ __forceinline__ float half_swap_sum(float x) { return x + xor32(x); }
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
   constexpr int NW = 4, BM = 128;
-  constexpr int KRB = 2 * D;          // bytes per K row
-  constexpr int KRP = 256 / KRB;      // K rows per 256-byte bank period
-  constexpr int KCPR = KRB / 16;      // 16-byte chunks per K row
-  constexpr int TB = kBN * KRB;       // bytes of a K tile (== bytes of a V^T tile: D rows x 64 keys)
-  constexpr int NI = TB / 1024 / NW;  // 1-KB direct loads per wave, per tile and tensor
+  constexpr int KP = 2 * D + 16;          // LDS pitch of a K row (bytes): data + one 16-byte pad
+  constexpr int VP = 2 * kBN + 16;        // LDS pitch of a V^T row (64 keys + pad)
+  constexpr int KT_B = kBN * KP, VT_B = D * VP;
+  constexpr int KBLK = KT_B / 1024, VBLK = VT_B / 1024;  // 1-KB direct loads per tile
+  constexpr int KI = (KBLK + NW - 1) / NW, VI = (VBLK + NW - 1) / NW;
+  constexpr int KCPR = 2 * D / 16;        // data chunks per K row
   constexpr int KSTEPS = D / 16, MBLK = D / 32;
-  // [buffer][K tile | V^T tile].  K row r keeps 16-byte chunk c at c ^ ((r / KRP) % KCPR);
-  // V^T row d (64 keys, 128 bytes) keeps chunk c at c ^ ((d / 2) % 8): the A-operand reads of
-  // both products then touch every bank once per 16 lanes.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];
+  static_assert(KT_B % 1024 == 0 && VT_B % 1024 == 0, "tiles must be whole 1-KB blocks");
+  // [K stage 0 | K stage 1 | V^T stage 0 | V^T stage 1].  A padded pitch of 68 (K) or 36 (V^T)
+  // dwords puts the 16 rows a 16-lane group reads on 16 distinct 4-bank groups, so both
+  // products read conflict-free with addresses that are a lane constant plus an immediate.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KT_B + 2 * VT_B];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -360,7 +366,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
   const int tile = xcd_remap(blockIdx.x, n_qt * a.H);
   const int h = tile / n_qt, qt = tile - h * n_qt;
   const int q_base = qt * BM + wave * 32;
+  const float sl2 = a.sl2;
 
+  // Q^T, pre-multiplied by softmax scale * log2(e): scores come out in log2 units.
   bf16x8_t qreg[KSTEPS];
   {
     const int qi = q_base + l32;
@@ -369,6 +377,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       u32x4_t v = ok ? *(const u32x4_t*)(qp + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(bf16_lo_to_f32(v[e]) * sl2, bf16_hi_to_f32(v[e]) * sl2);
       qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -377,167 +387,220 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
   for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
+  f32x16_t negm;  // -m_run in every entry: the accumulator the score product starts from
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
 
-  int cseg = 0, coff = 0;
-  auto skip_empty = [&]() {
-    while (cseg < a.nseg && coff >= a.seg[cseg].n) {
-      ++cseg;
-      coff = 0;
-    }
+  // Lane-constant parts of the direct loads.  Lane l of block blk fills LDS bytes
+  // [blk*1024 + 16 l, +16); lanes that land on a pad chunk fetch a harmless valid chunk.
+  int kq_row[KI], kq_c16[KI], vq_row[VI], vq_chk[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int ob = (wave + NW * i) * 1024 + 16 * lane;
+    int row = ob / KP, ch = (ob % KP) / 16;
+    if (ch >= KCPR || row >= kBN) row = 0, ch = 0;
+    kq_row[i] = row;
+    kq_c16[i] = 16 * ch;
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int ob = (wave + NW * i) * 1024 + 16 * lane;
+    int d = ob / VP, ch = (ob % VP) / 16;
+    if (ch >= 8 || d >= D) d = 0, ch = 0;
+    vq_row[i] = d;
+    vq_chk[i] = ch;
+  }
+
+  // Two uniform tile iterators over the key ranges: K runs ahead of V.
+  int n_tiles = 0;
+  for (int s_ = 0; s_ < a.nseg; ++s_) n_tiles += (a.seg[s_].n + kBN - 1) / kBN;
+  if (n_tiles == 0) return;  // no keys: the host never launches this
+  int ksi = 0, krem = 0, k_rs_b = 0;
+  const uint8_t* kp = nullptr;
+  auto k_seg = [&](int s_) {
+    const KvSeg sg = a.seg[s_];
+    kp = (const uint8_t*)sg.k + 2 * (int64_t)h * sg.k_hs;
+    k_rs_b = (int)(2 * sg.k_rs);
+    krem = sg.n;
   };
-  skip_empty();
-  if (cseg >= a.nseg) return;  // no keys: the host never launches this
+  int vsi = 0, vrem = 0, v_ds_b = 0, v_al16 = 1;
+  const uint8_t* vp = nullptr;
+  auto v_seg = [&](int s_) {
+    const KvSeg sg = a.seg[s_];
+    vp = (const uint8_t*)sg.v + 2 * (int64_t)h * sg.v_hs;
+    v_ds_b = (int)(2 * sg.v_ds);
+    vrem = sg.n;
+    v_al16 = sg.v_al16;
+  };
+  k_seg(0);
+  while (krem <= 0 && ++ksi < a.nseg) k_seg(ksi);
+  v_seg(0);
+  while (vrem <= 0 && ++vsi < a.nseg) v_seg(vsi);
 
-  // Issue the loads of one K tile and one V^T tile into buffer b; returns the valid key count.
-  auto issue = [&](int b, int si, int off) -> int {
-    const KvSeg sg = a.seg[si];
-    const int nk = sg.n - off < kBN ? sg.n - off : kBN;
-    uint8_t* kt = smem + b * 2 * TB;
-    uint8_t* vt = kt + TB;
-    const uint8_t* kg = (const uint8_t*)sg.k + 2 * (h * sg.k_hs + (int64_t)off * sg.k_rs);
+  // Issue the next K tile into stage st; returns its valid key count.
+  auto issue_k = [&](int st) -> int {
+    const int nk = krem < kBN ? krem : kBN;
+    uint8_t* dst = smem + st * KT_B;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int blk = wave * NI + i;
-      const int ob = blk * 1024 + lane * 16;
-      const int r = ob / KRB, p = (ob % KRB) / 16;
-      const int c = p ^ ((r / KRP) % KCPR);
-      const int rr = r < nk ? r : 0;  // rows past the range: any valid row (scores are masked)
-      __builtin_amdgcn_global_load_lds(kg + 2 * (int64_t)rr * sg.k_rs + 16 * c, lds_ptr(kt + blk * 1024), 16, 0, 0);
+    for (int i = 0; i < KI; ++i) {
+      const int blk = wave + NW * i;
+      if (blk < KBLK) {
+        const int rr = kq_row[i] < nk ? kq_row[i] : 0;  // rows past the range: a valid row (masked)
+        __builtin_amdgcn_global_load_lds(kp + (uint32_t)(rr * k_rs_b + kq_c16[i]), lds_ptr(dst + blk * 1024), 16, 0,
+                                         0);
+      }
     }
-    const uint8_t* vg = (const uint8_t*)sg.v + 2 * (h * sg.v_hs + (int64_t)off);
-    if (sg.v_al16) {
+    krem -= kBN;
+    kp += kBN * k_rs_b;
+    while (krem <= 0 && ++ksi < a.nseg) k_seg(ksi);
+    return nk;
+  };
+  // Issue the next V^T tile into stage st.
+  auto issue_v = [&](int st) {
+    const int nk = vrem < kBN ? vrem : kBN;
+    uint8_t* dst = smem + 2 * KT_B + st * VT_B;
+    if (v_al16) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int blk = wave * NI + i;
-        const int ob = blk * 1024 + lane * 16;
-        const int d = ob / 128, p = (ob % 128) / 16;
-        const int c = p ^ ((d >> 1) & 7);
-        const int cc = 8 * c < nk ? c : 0;  // chunks past the range: any valid chunk (P is 0 there)
-        __builtin_amdgcn_global_load_lds(vg + 2 * (int64_t)d * sg.v_ds + 16 * cc, lds_ptr(vt + blk * 1024), 16,
-                                         0, 0);
+      for (int i = 0; i < VI; ++i) {
+        const int blk = wave + NW * i;
+        if (blk < VBLK) {
+          const int cc = 8 * vq_chk[i] < nk ? vq_chk[i] : 0;  // chunks past the range: valid data, P is 0
+          __builtin_amdgcn_global_load_lds(vp + (uint32_t)(vq_row[i] * v_ds_b + 16 * cc),
+                                           lds_ptr(dst + blk * 1024), 16, 0, 0);
+        }
       }
     } else {
       // ranges whose keys are not 16-byte aligned: element copies through registers
       for (int idx = tid; idx < D * kBN; idx += NW * 64) {
         const int d = idx / kBN, e = idx % kBN;
-        const int key = 8 * ((e / 8) ^ ((d >> 1) & 7)) + (e % 8);
-        const int kk = key < nk ? key : 0;
-        ((uint16_t*)(vt + d * 128))[e] = ((const uint16_t*)vg)[(int64_t)d * sg.v_ds + kk];
+        const int kk = e < nk ? e : 0;
+        ((uint16_t*)(dst + d * VP))[e] = *(const uint16_t*)(vp + (int64_t)d * v_ds_b + 2 * kk);
       }
     }
-    return nk;
+    vrem -= kBN;
+    vp += 2 * kBN;
+    while (vrem <= 0 && ++vsi < a.nseg) v_seg(vsi);
   };
 
-  int nk_cur = issue(0, cseg, coff);
-  coff += kBN;
-  skip_empty();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // per-lane LDS byte offsets of the A operands (plus immediates per k-step)
+  int koff[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) koff[kb] = (kb * 32 + k_row_perm(l32)) * KP + 16 * hf;
+  const int voff = l32 * VP + 16 * hf;
+  const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  // per-lane LDS byte offsets of the A operands
-  int krow_off[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) krow_off[kb] = (kb * 32 + k_row_perm(l32)) * KRB;
-  int kswz[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) kswz[kb] = ((kb * 32 + k_row_perm(l32)) / KRP) % KCPR;
-  const int vswz = (l32 >> 1) & 7;  // (d / 2) % 8 for d = 32*mb + l32
+  // prologue: K0, V0, K1 in flight
+  int nk_k[2];
+  nk_k[0] = issue_k(0);
+  issue_v(0);
+  if (n_tiles > 1) nk_k[1] = issue_k(1);
 
-  const float sl2 = a.sl2;
-  int buf = 0;
-  while (true) {
-    const bool has_next = cseg < a.nseg;
-    int nk_next = 0;
-    if (has_next) {
-      nk_next = issue(buf ^ 1, cseg, coff);
-      coff += kBN;
-      skip_empty();
-    }
-    const uint8_t* kt = smem + buf * 2 * TB;
-    const uint8_t* vt = kt + TB;
+  for (int t = 0; t < n_tiles; ++t) {
+    const int st = t & 1;
+    const bool more = t + 1 < n_tiles;
+    // K_t landed (V_t and K_{t+1} may still be in flight), then everyone's V_{t-1} reads are done.
+    // Explicit waits + barrier: a fenced barrier would also wait for the loads still in flight.
+    if (more)
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (more) issue_v(st ^ 1);
 
-    // ---- S^T = K Q^T
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    // ---- S'^T = K (Q^T * scale * log2 e) - m_run
+    const uint8_t* kt = smem + st * KT_B;
+    f32x16_t s0 = negm, s1 = negm;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int c = 2 * ks + hf;
-        const bf16x8_t av = ld_bf16x8(kt + krow_off[kb] + ((c ^ kswz[kb]) << 4));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], s[kb], 0, 0, 0);
-      }
+      const bf16x8_t a0 = ld_bf16x8(kt + koff[0] + 32 * ks);
+      const bf16x8_t a1 = ld_bf16x8(kt + koff[1] + 32 * ks);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
     }
-    if (nk_cur < kBN) {
+    const int nk = nk_k[st];
+    if (nk < kBN) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + score_key(r, hf) >= nk_cur) s[kb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        if (score_key(r, hf) >= nk) s0[r] = -INFINITY;
+        if (32 + score_key(r, hf) >= nk) s1[r] = -INFINITY;
+      }
     }
 
-    // ---- online softmax; P^T packed to bf16 in the B-operand order
+    // ---- P = exp2(S'), packed to bf16 in the B-operand order; row sums of the bf16 values.
+    // The running max is raised only when some score exceeds it by a lot (first tile, or a
+    // row sum past 2^60): the result is the same for any max, and P stays far below overflow.
     bf16x8_t pb[4];
-    {
-      float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-      mx = fmaxf(mx, xor32(mx)) * sl2;
-      if (__any(mx > m_run + 8.0f)) {
-        const float mn = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-        m_run = mn;
-        l_run *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-      }
-      const float mneg = -m_run;
-      float lsum = 0.f;
+    float lsum = 0.f;
+    auto exp_pack = [&](float sub) {
+      lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        const f32x16_t& sv = kb ? s1 : s0;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           u32x4_t pk;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 8 * half + 2 * e;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, mneg));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], sl2, mneg));
-            lsum += p0 + p1;
-            pk[e] = pack_bf16x2(p0, p1);
+            const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sv[r] - sub), __builtin_amdgcn_exp2f(sv[r + 1] - sub));
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, one2),
+                                                   lsum, false);
+            pk[e] = w;
           }
           pb[2 * kb + half] = __builtin_bit_cast(bf16x8_t, pk);
         }
       }
-      l_run += lsum;
+    };
+    bool raise = t == 0;
+    if (!raise) {
+      exp_pack(0.f);
+      raise = __any(lsum > 0x1p60f);
     }
+    if (raise) {
+      float ma = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+      float mb_ = fmaxf(fmaxf(s1[0], s1[1]), s1[2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) {
+        ma = fmaxf(fmaxf(ma, s0[r]), s0[r + 1]);
+        mb_ = fmaxf(fmaxf(mb_, s1[r]), s1[r + 1]);
+      }
+      float mx = fmaxf(fmaxf(ma, s0[15]), fmaxf(mb_, s1[15]));
+      mx = half_swap_max(mx);
+      // first tile: m_run = max; later: only ever raise it
+      const float up = t == 0 ? mx : fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-up);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+      m_run += up;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[r] = -m_run;
+      exp_pack(up);
+    }
+    l_run += lsum;
+
+    // V_t landed (K_{t+1} and V_{t+1} may still be in flight), then everyone's K_t reads are done
+    if (more)
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 2 < n_tiles) nk_k[st] = issue_k(st);
 
     // ---- O^T += V^T P^T
+    const uint8_t* vt = smem + 2 * KT_B + st * VT_B;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int stp = 0; stp < 4; ++stp) {
 #pragma unroll
       for (int mb = 0; mb < MBLK; ++mb) {
-        const int c = 2 * st + hf;
-        const bf16x8_t av = ld_bf16x8(vt + (mb * 32 + l32) * 128 + ((c ^ vswz) << 4));
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[st], o[mb], 0, 0, 0);
+        const bf16x8_t av = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[stp], o[mb], 0, 0, 0);
       }
     }
-
-    if (!has_next) break;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    buf ^= 1;
-    nk_cur = nk_next;
   }
 
-  const float lt = l_run + xor32(l_run);
-  const float inv = 1.f / lt;
+  const float inv = 1.f / half_swap_sum(l_run);
   const int qi = q_base + l32;
   if (qi < a.Lq) {
     uint16_t* op = (uint16_t*)a.out + ((int64_t)qi * a.H + h) * D + 4 * hf;
