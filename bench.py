@@ -32,11 +32,14 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="abot720")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--pool", type=int, default=2, help="device-resident input sets cycled over steps")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after timing, copy the cache out once (plain row copies of known size) so that "
+                         "counter passes can scale FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -115,8 +118,10 @@ class Runner:
                 cache.rope_apply(q, out=self.qr, start_frame=t)
                 cache.rope_apply(k, out=self.kr[li], start_frame=t)
                 self._ev("rope1")
+                self._ev("stage0")
+                cache.stage_v(v)
                 self._ev("attn0")
-                cache.chunk_attention(self.qr, self.kr[li], v, out=self.out)
+                cache.chunk_attention(self.qr, self.kr[li], None, out=self.out)
                 self._ev("attn1")
                 if wl.text_tokens:
                     self._ev("cross0")
@@ -127,6 +132,14 @@ class Runner:
                     cache.append_evict(k if self.rel else self.kr[li], v)
                     self._ev("app1")
         self._ev("step1")
+        self.chunk += 1
+
+    def fill_step(self):
+        """Advance the cache by one chunk (write-back only): builds the steady state without attention."""
+        _, k, v = self.pool[self.chunk % len(self.pool)][self.wl.passes - 1]
+        for li, cache in enumerate(self.caches):
+            kk = k if self.rel else cache.rope_apply(k, out=self.kr[li], start_frame=cache.info().n_appended)
+            cache.append_evict(kk, v)
         self.chunk += 1
 
     def visible(self):
@@ -203,13 +216,13 @@ def main():
     torch.cuda.set_device(0)
     r = Runner(wl, max(1, args.pool))
     r.prefill()
-    while r.visible() < cfg.window_frames:   # fill the window (not timed)
-        r.step()
+    while r.visible() < cfg.window_frames:   # fill the window (not timed, no attention launches)
+        r.fill_step()
     for _ in range(args.warmup):
         r.step()
     torch.cuda.synchronize()
-    r.ev = {k: [] for k in ("step0", "step1", "win0", "win1", "rope0", "rope1", "attn0", "attn1", "cross0",
-                            "cross1", "app0", "app1")}
+    r.ev = {k: [] for k in ("step0", "step1", "win0", "win1", "rope0", "rope1", "stage0", "attn0", "attn1",
+                            "cross0", "cross1", "app0", "app1")}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -218,7 +231,11 @@ def main():
     wall = time.perf_counter() - t0
     ev = r.ev
     ms_step = wall * 1e3 / args.steps
+    if args.calibrate:
+        r.caches[0].gather()   # K rows: n_cached*F*H*D elements read and written by copy_frames_kernel
+        torch.cuda.synchronize()
     attn_ms, _ = avg_ms(ev, "attn0", "attn1")
+    stage_ms, _ = avg_ms(ev, "stage0", "attn0")
     app_ms, _ = avg_ms(ev, "app0", "app1")
     rope_ms, _ = avg_ms(ev, "rope0", "rope1")
     win_ms, _ = avg_ms(ev, "win0", "win1")
@@ -237,7 +254,7 @@ def main():
     peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_VECTOR_PEAK_TFLOPS
     roof = {"bound": "mfma" if bf16 else "alu", "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(attn_tflops / peak, 4),
-            "traffic": traffic_from_profile(wl.name, None), "kernel": "attn_bf16_kernel" if bf16 else "attn_f32_kernel",
+            "traffic": traffic_from_profile(wl.name, None), "kernel": "attn_bf16_vt_kernel" if bf16 else "attn_f32_kernel",
             "avg_kernel_ms": round(attn_ms, 4), "algorithmic_flop_per_launch": attn_flop}
     out = {
         "metric": "chunk-attention TFLOP/s + % bf16 MFMA peak; cache-update GB/s; per-chunk ms",
@@ -259,6 +276,7 @@ def main():
                          "frac_hbm": round(app_bytes / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "avg_us": round(app_ms * 1e3, 2), "bytes": app_bytes},
         "rope_qk": {"GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1), "avg_us": round(rope_ms * 1e3, 2)},
+        "stage_v": {"GB/s": round(2 * lq * h * d * elt / (stage_ms * 1e-3) / 1e9, 1), "avg_us": round(stage_ms * 1e3, 2)},
         "per_chunk_ms": {"mean": round(float(np.mean(steps_ms)), 4), "p50": round(float(np.median(steps_ms)), 4),
                          "p99": round(float(np.percentile(steps_ms, 99)), 4)},
     }

@@ -90,10 +90,12 @@ int skv_abi_version(void);
 const char* skv_status_string(skv_status s);
 
 /* Bytes the caller must allocate for one K store and one V store (each
- * W*F*H*D elements of cfg->dtype) and for the REL window workspace
- * ((W-c)*F*H*D elements; 0 in ABS mode).  Physical layout of a store:
- * [H][W*F][D] (head-major); slot s holds tokens [s*F, (s+1)*F).  Frame f < S
- * lives in slot f, frame f >= S in slot S + (f-S) mod (W-S). */
+ * W*F*H*D elements of cfg->dtype) and for the workspace.  Physical layouts:
+ *   K store  [H][W*F][D]   (head-major; slot s holds tokens [s*F, (s+1)*F));
+ *   V store  [H][D][W*F]   (transposed per head, same token numbering);
+ *   workspace: REL only, the rotated visible window [H][(W-c)*F][D], then the
+ *   staged current-chunk values [H][D][P] with P = c*F rounded up to 64.
+ * Frame f < S lives in slot f, frame f >= S in slot S + (f-S) mod (W-S). */
 skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_t* workspace_bytes);
 
 /* Bind caller-allocated stores (and, in REL mode, the workspace) to a new
@@ -131,9 +133,18 @@ skv_status rope_apply(const skv_cache* cache, const void* x_in, void* x_out, int
  * chunk; its result serves every pass until the next append or reset. */
 skv_status rope_apply_window(skv_cache* cache, void* stream);
 
+/* Stage the current chunk's values v_cur [c*F, H, D] in the workspace, in the
+ * transposed layout the attention kernel reads (V^T[h][d][token], rows padded
+ * with zeros to a multiple of 64 tokens).  chunk_attention does this itself when
+ * it is given v_cur; calling it separately lets a caller time or overlap it.
+ * n_frames must equal c. */
+skv_status kv_cache_stage_v(skv_cache* cache, const void* v_cur, int32_t n_frames, void* stream);
+
 /* Chunk attention ([LB-fast] 3. KV 缓存 滚动窗口: attention over the window
  * slice; [ABot-stream] 机制二: block-causal, frames of a chunk see each other).
- * q, k_cur, v_cur: [c*F, H, D], q and k_cur already rotated with rope_apply.
+ * q, k_cur, v_cur: [c*F, H, D], q and k_cur already rotated with rope_apply;
+ * v_cur may be NULL to use the values staged by kv_cache_stage_v (since the
+ * last append or reset; SKV_ERR_STATE otherwise).
  * out[i] = softmax(q_i . K^T / sqrt(D)) V over the visible keys: the visible
  * sink frames, the visible ring frames, and the current chunk.  The cache is
  * read only.  fp32 softmax and accumulation; out in cfg dtype.  n_frames must

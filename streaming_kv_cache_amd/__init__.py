@@ -3,7 +3,7 @@
 Every step of the hot path runs in the library's HIP kernels.  torch is used for
 device memory (the stores, the workspace, inputs and outputs) and for the
 current HIP stream.  Importing this package fails loudly when the library has
-not been built (``python -m streaming_kv_cache_amd.build``); there is no
+not been built (``python streaming_kv_cache_amd/build.py``); there is no
 fallback implementation.
 """
 from __future__ import annotations
@@ -24,7 +24,7 @@ ROPE_ABS, ROPE_REL = 0, 1
 EXPORTED = (
     "skv_abi_version", "skv_status_string", "kv_cache_bytes", "kv_cache_init", "kv_cache_reset",
     "kv_cache_destroy", "kv_cache_append_evict", "rope_apply", "rope_apply_window", "chunk_attention",
-    "cross_attention", "kv_cache_info", "kv_cache_gather",
+    "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v",
 )
 
 
@@ -55,7 +55,7 @@ class SkvError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m streaming_kv_cache_amd.build`")
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python streaming_kv_cache_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
     sig = {
@@ -73,6 +73,7 @@ def _load() -> ctypes.CDLL:
         "cross_attention": ([vp, i32, vp, vp, i32, i32, i32, i32, vp, vp], st),
         "kv_cache_info": ([vp, ctypes.POINTER(KvCacheInfo)], st),
         "kv_cache_gather": ([vp, vp, vp, ctypes.POINTER(ctypes.c_int64), vp], st),
+        "kv_cache_stage_v": ([vp, vp, i32, vp], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -207,12 +208,19 @@ class KVCache:
     def rope_apply_window(self, stream=None) -> None:
         _check(lib.rope_apply_window(self._h, _stream(stream)), "rope_apply_window")
 
-    def chunk_attention(self, q: torch.Tensor, k_cur: torch.Tensor, v_cur: torch.Tensor,
+    def stage_v(self, v_cur: torch.Tensor, stream=None) -> None:
+        c = self.cfg.chunk_frames
+        self._tensor(v_cur, c, "v_cur")
+        _check(lib.kv_cache_stage_v(self._h, _ptr(v_cur), c, _stream(stream)), "kv_cache_stage_v")
+
+    def chunk_attention(self, q: torch.Tensor, k_cur: torch.Tensor, v_cur: Optional[torch.Tensor],
                         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """v_cur=None uses the values staged by stage_v."""
         c = self.cfg.chunk_frames
         self._tensor(q, c, "q")
         self._tensor(k_cur, c, "k_cur")
-        self._tensor(v_cur, c, "v_cur")
+        if v_cur is not None:
+            self._tensor(v_cur, c, "v_cur")
         out = torch.empty_like(q) if out is None else self._tensor(out, c, "out")
         _check(lib.chunk_attention(self._h, _ptr(q), _ptr(k_cur), _ptr(v_cur), c, _ptr(out), _stream(stream)),
                "chunk_attention")

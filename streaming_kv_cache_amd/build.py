@@ -1,4 +1,7 @@
-"""Build the HIP library ``libskv.so`` for gfx950 in-tree (run: python -m streaming_kv_cache_amd.build)."""
+"""Build the HIP library ``libskv.so`` for gfx950 in-tree (run: python streaming_kv_cache_amd/build.py).
+
+Run as a script or load by path: importing the package itself requires the built library.
+"""
 from __future__ import annotations
 
 import concurrent.futures as cf

@@ -84,9 +84,12 @@ hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], int n_
 // [LB-src] 改造③ / [LB-causal] "Attention Sink" (start_frame offset) and
 // [ABot-stream] 机制三 (relative ids over the visible window): token (frame i,
 // row r, col w) turns pair k of the [time | height | width] part of head_dim by
-// position * omega_k.  cos/sin are computed once per (token, pair) in fp64 and
-// reused for every head; the rotation itself is fp32.
+// position * omega_k.  A block owns a few tokens and a group of kRopeHeads heads:
+// each thread computes cos/sin for its 4 pairs once (angle reduced mod 2*pi in
+// fp64, then fp32 sincos) and applies them to every head of the group, issuing
+// all of its loads before the first store.
 constexpr int kRopeThreads = 256;
+constexpr int kRopeHeads = 8;
 
 struct RopeArgs {
   TokView src, dst;
@@ -101,44 +104,52 @@ struct RopeArgs {
 };
 
 template <typename T>
-__device__ __forceinline__ void rope_row(const T* __restrict__ s, T* __restrict__ d, const float (&cs)[4],
-                                         const float (&sn)[4]);
+struct RopeIo;
 
 template <>
-__device__ __forceinline__ void rope_row<float>(const float* __restrict__ s, float* __restrict__ d,
-                                                const float (&cs)[4], const float (&sn)[4]) {
-  const f32x4_t a = *(const f32x4_t*)s, b = *(const f32x4_t*)(s + 4);
-  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  float y[8];
+struct RopeIo<__bf16> {
+  typedef u32x4_t V;  // 8 elements
+  static __device__ __forceinline__ V load(const __bf16* p) { return *(const V*)p; }
+  static __device__ __forceinline__ void rot_store(__bf16* d, const V& w, const float (&cs)[4], const float (&sn)[4]) {
+    u32x4_t o;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    y[2 * p] = x[2 * p] * cs[p] - x[2 * p + 1] * sn[p];
-    y[2 * p + 1] = x[2 * p] * sn[p] + x[2 * p + 1] * cs[p];
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = bf16_lo_to_f32(w[p]), x1 = bf16_hi_to_f32(w[p]);
+      o[p] = pack_bf16x2(x0 * cs[p] - x1 * sn[p], x0 * sn[p] + x1 * cs[p]);
+    }
+    *(u32x4_t*)d = o;
   }
-  *(f32x4_t*)d = f32x4_t{y[0], y[1], y[2], y[3]};
-  *(f32x4_t*)(d + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
-}
+};
 
 template <>
-__device__ __forceinline__ void rope_row<__bf16>(const __bf16* __restrict__ s, __bf16* __restrict__ d,
-                                                 const float (&cs)[4], const float (&sn)[4]) {
-  const u32x4_t w = *(const u32x4_t*)s;
-  u32x4_t o;
+struct RopeIo<float> {
+  struct V {
+    f32x4_t a, b;
+  };
+  static __device__ __forceinline__ V load(const float* p) { return V{*(const f32x4_t*)p, *(const f32x4_t*)(p + 4)}; }
+  static __device__ __forceinline__ void rot_store(float* d, const V& v, const float (&cs)[4], const float (&sn)[4]) {
+    const float x[8] = {v.a[0], v.a[1], v.a[2], v.a[3], v.b[0], v.b[1], v.b[2], v.b[3]};
+    float y[8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float x0 = bf16_lo_to_f32(w[p]), x1 = bf16_hi_to_f32(w[p]);
-    o[p] = pack_bf16x2(x0 * cs[p] - x1 * sn[p], x0 * sn[p] + x1 * cs[p]);
+    for (int p = 0; p < 4; ++p) {
+      y[2 * p] = x[2 * p] * cs[p] - x[2 * p + 1] * sn[p];
+      y[2 * p + 1] = x[2 * p] * sn[p] + x[2 * p + 1] * cs[p];
+    }
+    *(f32x4_t*)d = f32x4_t{y[0], y[1], y[2], y[3]};
+    *(f32x4_t*)(d + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
   }
-  *(u32x4_t*)d = o;
-}
+};
 
 template <typename T>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeArgs a) {
+  using IO = RopeIo<T>;
   const int G = a.D >> 3;                 // groups of 4 pairs (8 elements) per row
   const int tpb = kRopeThreads / G;       // tokens per block
   const int g = threadIdx.x % G, tl = threadIdx.x / G;
   const int gt = blockIdx.x * tpb + tl;   // token index in the launch
   if (gt >= a.n_tok) return;
+  const int h0 = blockIdx.y * kRopeHeads;
+  const int nh = a.H - h0 < kRopeHeads ? a.H - h0 : kRopeHeads;
   const int fi = gt / a.F, tok = gt - fi * a.F;
   int sf = 0, df = 0;
   for (int r = 0; r < a.nruns; ++r) {
@@ -148,22 +159,28 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeArgs a) {
       df = run.dst0 + (fi - run.start);
     }
   }
+  const T* s = (const T*)a.src.base + (int64_t)(sf * a.F + tok) * a.src.tok_stride + g * 8 + h0 * a.src.head_stride;
+  T* d = (T*)a.dst.base + (int64_t)(df * a.F + tok) * a.dst.tok_stride + g * 8 + h0 * a.dst.head_stride;
+  typename IO::V x[kRopeHeads];
+#pragma unroll
+  for (int i = 0; i < kRopeHeads; ++i)
+    if (i < nh) x[i] = IO::load(s + i * a.src.head_stride);
   int64_t t = a.t0 + fi;
   if (a.clamp_max >= 0) t = t < 0 ? 0 : (t > a.clamp_max ? a.clamp_max : t);
   const int row = tok / a.gw, col = tok - row * a.gw;
   float cs[4], sn[4];
+  const double two_pi = 6.283185307179586476925287;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int pair = g * 4 + p;
     const double pos = pair < a.pair_h ? (double)t : (pair < a.pair_w ? (double)row : (double)col);
-    double sd, cd;
-    sincos(pos * a.omega[pair], &sd, &cd);
-    cs[p] = (float)cd;
-    sn[p] = (float)sd;
+    const double ang = pos * a.omega[pair];
+    const double red = ang - two_pi * rint(ang / two_pi);  // |red| <= pi
+    sincosf((float)red, &sn[p], &cs[p]);
   }
-  const T* s = (const T*)a.src.base + (int64_t)(sf * a.F + tok) * a.src.tok_stride + g * 8;
-  T* d = (T*)a.dst.base + (int64_t)(df * a.F + tok) * a.dst.tok_stride + g * 8;
-  for (int h = 0; h < a.H; ++h) rope_row<T>(s + h * a.src.head_stride, d + h * a.dst.head_stride, cs, sn);
+#pragma unroll
+  for (int i = 0; i < kRopeHeads; ++i)
+    if (i < nh) IO::rot_store(d + i * a.dst.head_stride, x[i], cs, sn);
 }
 
 hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream) {
@@ -189,7 +206,7 @@ hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream) {
   for (; p < 64; ++p) a.omega[p] = 0.0;
   const int G = L.D / 8;
   const int tpb = kRopeThreads / G;
-  dim3 grid((a.n_tok + tpb - 1) / tpb);
+  dim3 grid((a.n_tok + tpb - 1) / tpb, (L.H + kRopeHeads - 1) / kRopeHeads);
   if (L.dtype_bf16)
     hipLaunchKernelGGL(rope_kernel<__bf16>, grid, dim3(kRopeThreads), 0, stream, a);
   else

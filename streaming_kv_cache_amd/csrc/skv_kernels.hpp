@@ -11,13 +11,19 @@ namespace skv {
 hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], int n_tensors, const FrameRun* runs,
                               int nruns, int n_frames, int F, int H, int D, int elt, hipStream_t stream);
 
-// Token-major <-> transposed V (V^T[h][d][key]).  runs map launch frames to
-// frame positions in V^T key space (dst0); nruns == 0 means key = token and a
-// zero-filled row tail up to row_pad keys (tok_to_vt only).
-struct VtCopyArgs {
-  void* tok_base;
+// Write-back of whole frames (K rows + transposed V) and current-chunk staging.
+// Sources are token-major [tokens, H, D] (token t, head h at t*tok_stride + h*head_stride).
+// K store: head h, key j at k_dst + h*k_hs + j*D.  V^T: (h, d, key j) at vt_dst + h*vt_hs +
+// d*vt_ds + j.  runs map launch frames to their key-space frame (slot) in dst0; nruns == 0
+// means key = token, and the V^T rows are written (zero-filled) up to row_pad keys.
+// k_src == nullptr writes V only.  vt_to_tok reads vt_dst and writes token-major rows to k_dst.
+struct WriteArgs {
+  const void* k_src;
+  const void* v_src;
   int64_t tok_stride, head_stride;
-  void* vt_base;
+  void* k_dst;
+  int64_t k_hs;
+  void* vt_dst;
   int64_t vt_hs, vt_ds;
   FrameRun runs[3];
   int32_t nruns;
@@ -25,8 +31,8 @@ struct VtCopyArgs {
   int32_t n_tok;
   int32_t row_pad;
 };
-hipError_t launch_tok_to_vt(const VtCopyArgs& a, int elt, hipStream_t stream);
-hipError_t launch_vt_to_tok(const VtCopyArgs& a, int elt, hipStream_t stream);
+hipError_t launch_write_kv(const WriteArgs& a, int elt, hipStream_t stream);
+hipError_t launch_vt_to_tok(const WriteArgs& a, int elt, hipStream_t stream);
 
 struct RopeLaunch {
   TokView src, dst;

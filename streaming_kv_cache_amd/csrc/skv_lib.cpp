@@ -17,6 +17,7 @@ struct skv_cache {
   void* v_store = nullptr;
   void* ws = nullptr;
   bool window_ready = false;
+  bool v_staged = false;  // current-chunk values staged since the last append/reset
   bool poisoned = false;
 };
 
@@ -64,9 +65,40 @@ int64_t ws_window_elems(const skv::Geometry& g) { return skv::workspace_elems(g)
 int64_t ws_total_elems(const skv::Geometry& g) { return ws_window_elems(g) + (int64_t)g.H * g.D * cur_row(g); }
 void* ws_vt(const skv_cache* c) { return (char*)c->ws + ws_window_elems(c->g) * c->g.elt; }
 
+// Current chunk's V -> V^T rows in the workspace (tail zero-filled to a multiple of 64 keys).
+skv_status stage_v(skv_cache* c, const void* v_cur, void* stream) {
+  const skv::Geometry& g = c->g;
+  skv::WriteArgs wa{};
+  wa.k_src = nullptr;
+  wa.v_src = v_cur;
+  wa.tok_stride = (int64_t)g.H * g.D;
+  wa.head_stride = g.D;
+  wa.vt_dst = ws_vt(c);
+  wa.vt_hs = (int64_t)g.D * cur_row(g);
+  wa.vt_ds = cur_row(g);
+  wa.nruns = 0;
+  wa.F = g.F;
+  wa.H = g.H;
+  wa.D = g.D;
+  wa.n_tok = g.c * g.F;
+  wa.row_pad = (int32_t)cur_row(g);
+  return launched(c, skv::launch_write_kv(wa, g.elt, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+skv_status kv_cache_stage_v(skv_cache* c, const void* v_cur, int32_t n_frames, void* stream) {
+  skv_status st = check_handle(c);
+  if (st != SKV_OK) return st;
+  if ((st = check_ptr(v_cur)) != SKV_OK) return st;
+  if (n_frames != c->g.c) return SKV_ERR_SHAPE;
+  st = stage_v(c, v_cur, stream);
+  if (st == SKV_OK) c->v_staged = true;
+  return st;
+}
+
 
 int skv_abi_version(void) { return SKV_ABI_VERSION; }
 
@@ -115,6 +147,7 @@ skv_status kv_cache_reset(skv_cache* c) {
   if (!c) return SKV_ERR_NULL;
   c->ring.T = 0;
   c->window_ready = false;
+  c->v_staged = false;
   c->poisoned = false;
   return SKV_OK;
 }
@@ -157,29 +190,28 @@ skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int
       runs[nruns++] = skv::FrameRun{i, 1, i, slot};
     }
   }
-  const skv::TokView src[2] = {token_view(g, k), token_view(g, k)};
-  const skv::TokView dst[2] = {store_view(g, c->k_store), store_view(g, c->k_store)};
-  st = launched(c, skv::launch_copy_frames(src, dst, 1, runs, nruns, n_frames, g.F, g.H, g.D, g.elt,
-                                            (hipStream_t)stream));
-  if (st != SKV_OK) return st;
-  skv::VtCopyArgs va;
-  va.tok_base = const_cast<void*>(v);
-  va.tok_stride = (int64_t)g.H * g.D;
-  va.head_stride = g.D;
-  va.vt_base = c->v_store;
-  va.vt_hs = (int64_t)g.D * vt_row(g);
-  va.vt_ds = vt_row(g);
-  for (int i = 0; i < 3; ++i) va.runs[i] = i < nruns ? runs[i] : skv::FrameRun{0, 0, 0, 0};
-  va.nruns = nruns;
-  va.F = g.F;
-  va.H = g.H;
-  va.D = g.D;
-  va.n_tok = n_frames * g.F;
-  va.row_pad = 0;
-  st = launched(c, skv::launch_tok_to_vt(va, g.elt, (hipStream_t)stream));
+  skv::WriteArgs wa{};
+  wa.k_src = k;
+  wa.v_src = v;
+  wa.tok_stride = (int64_t)g.H * g.D;
+  wa.head_stride = g.D;
+  wa.k_dst = c->k_store;
+  wa.k_hs = (int64_t)g.W * g.F * g.D;
+  wa.vt_dst = c->v_store;
+  wa.vt_hs = (int64_t)g.D * vt_row(g);
+  wa.vt_ds = vt_row(g);
+  for (int i = 0; i < 3; ++i) wa.runs[i] = i < nruns ? runs[i] : skv::FrameRun{0, 0, 0, 0};
+  wa.nruns = nruns;
+  wa.F = g.F;
+  wa.H = g.H;
+  wa.D = g.D;
+  wa.n_tok = n_frames * g.F;
+  wa.row_pad = 0;
+  st = launched(c, skv::launch_write_kv(wa, g.elt, (hipStream_t)stream));
   if (st != SKV_OK) return st;
   c->ring.T += n_frames;
   c->window_ready = false;
+  c->v_staged = false;
   return SKV_OK;
 }
 
@@ -259,31 +291,20 @@ skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur
   if (st != SKV_OK) return st;
   if ((st = check_ptr(q)) != SKV_OK) return st;
   if ((st = check_ptr(k_cur)) != SKV_OK) return st;
-  if ((st = check_ptr(v_cur)) != SKV_OK) return st;
+  if (v_cur && misaligned(v_cur)) return SKV_ERR_ALIGN;
   if ((st = check_ptr(out)) != SKV_OK) return st;
   const skv::Geometry& g = c->g;
   if (n_frames != g.c) return SKV_ERR_SHAPE;
   const skv::VisiblePlan p = c->ring.plan(g, g.c);
   const bool rel = g.mode == SKV_ROPE_REL;
   if (rel && p.n_hist > 0 && !c->window_ready) return SKV_ERR_STATE;
+  if (!v_cur && !c->v_staged) return SKV_ERR_STATE;
 
-  // current chunk's V -> V^T rows in the workspace (tail zero-filled to a multiple of 64 keys)
-  skv::VtCopyArgs va;
-  va.tok_base = const_cast<void*>(v_cur);
-  va.tok_stride = (int64_t)g.H * g.D;
-  va.head_stride = g.D;
-  va.vt_base = ws_vt(c);
-  va.vt_hs = (int64_t)g.D * cur_row(g);
-  va.vt_ds = cur_row(g);
-  for (int i = 0; i < 3; ++i) va.runs[i] = skv::FrameRun{0, 0, 0, 0};
-  va.nruns = 0;
-  va.F = g.F;
-  va.H = g.H;
-  va.D = g.D;
-  va.n_tok = g.c * g.F;
-  va.row_pad = (int32_t)cur_row(g);
-  st = launched(c, skv::launch_tok_to_vt(va, g.elt, (hipStream_t)stream));
-  if (st != SKV_OK) return st;
+  if (v_cur) {
+    st = stage_v(c, v_cur, stream);
+    if (st != SKV_OK) return st;
+    c->v_staged = true;
+  }
 
   skv::AttnArgs a;
   a.q = q;
@@ -384,11 +405,11 @@ skv_status kv_cache_gather(const skv_cache* cc, void* k_out, void* v_out, int64_
   const skv::TokView dst[2] = {token_view(g, k_out), token_view(g, k_out)};
   st = launched(c, skv::launch_copy_frames(src, dst, 1, runs, nruns, n, g.F, g.H, g.D, g.elt, (hipStream_t)stream));
   if (st != SKV_OK) return st;
-  skv::VtCopyArgs va;
-  va.tok_base = v_out;
+  skv::WriteArgs va{};
+  va.k_dst = v_out;
   va.tok_stride = (int64_t)g.H * g.D;
   va.head_stride = g.D;
-  va.vt_base = c->v_store;
+  va.vt_dst = c->v_store;
   va.vt_hs = (int64_t)g.D * vt_row(g);
   va.vt_ds = vt_row(g);
   for (int i = 0; i < 3; ++i)

@@ -94,7 +94,10 @@ def test_init_validation_and_info():
     assert skv.lib.kv_cache_append_evict(h, ctypes.c_void_p(0x40004), p, 3, nul) == skv.ERR_ALIGN
     assert skv.lib.rope_apply(h, p, p, 2, 0, nul) == skv.ERR_SHAPE          # rel: n_frames must equal c
     assert skv.lib.chunk_attention(h, p, p, p, 2, p, nul) == skv.ERR_SHAPE
-    assert skv.lib.chunk_attention(h, p, p, nul, 3, p, nul) == skv.ERR_NULL
+    assert skv.lib.chunk_attention(h, nul, p, p, 3, p, nul) == skv.ERR_NULL
+    assert skv.lib.chunk_attention(h, p, p, nul, 3, p, nul) == skv.ERR_STATE   # nothing staged yet
+    assert skv.lib.kv_cache_stage_v(h, nul, 3, nul) == skv.ERR_NULL
+    assert skv.lib.kv_cache_stage_v(h, p, 2, nul) == skv.ERR_SHAPE
     assert skv.lib.kv_cache_gather(h, nul, p, None, nul) == skv.ERR_NULL
     assert skv.lib.kv_cache_reset(h) == skv.OK
     assert skv.lib.kv_cache_destroy(h) == skv.OK

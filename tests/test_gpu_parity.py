@@ -271,3 +271,25 @@ def test_full_size_sampled(name):
         say(f"  chunk {ch} pass {p}: max {e[0]:.3g} mean {e[1]:.3g} relrms {e[2]:.3g}")
         checked += 1
     assert checked == 6
+
+
+def test_staged_v_matches_direct():
+    """kv_cache_stage_v + chunk_attention(v_cur=NULL) gives the same bytes as passing v_cur."""
+    wl = WORKLOADS["small_rel"]
+    c = wl.cfg
+    say("[staged v] small_rel")
+    cache = skv.KVCache(c)
+    ro.prefill(wl, cache, None)
+    for ch in range(4):
+        cache.rope_apply_window()
+        q = cache.rope_apply(ro.draw(wl, c.chunk_frames, ch, 0, si.Q).cuda())
+        k = cache.rope_apply(ro.draw(wl, c.chunk_frames, ch, 0, si.K).cuda())
+        v = ro.draw(wl, c.chunk_frames, ch, 0, si.V).cuda()
+        direct = cache.chunk_attention(q, k, v)
+        cache.stage_v(v)
+        staged = cache.chunk_attention(q, k, None)
+        torch.cuda.synchronize()
+        assert torch.equal(direct, staged)
+        cache.append_evict(ro.draw(wl, c.chunk_frames, ch, 4, si.K).cuda(), v)
+    with pytest.raises(skv.SkvError):
+        cache.chunk_attention(q, k, None)   # append cleared the staged values
