@@ -148,7 +148,10 @@ skv_status kv_cache_stage_v(skv_cache* cache, const void* v_cur, int32_t n_frame
  * out[i] = softmax(q_i . K^T / sqrt(D)) V over the visible keys: the visible
  * sink frames, the visible ring frames, and the current chunk.  The cache is
  * read only.  fp32 softmax and accumulation; out in cfg dtype.  n_frames must
- * equal c.  REL mode with cached history requires rope_apply_window first. */
+ * equal c.  REL mode with cached history requires rope_apply_window first.
+ * bf16 runs one of two kernel shapes (4 or 8 waves per workgroup), chosen from
+ * the grid size; the environment variable SKV_ATTN_WAVES=4 or 8, read at each
+ * call, forces one of them (the two may round differently). */
 skv_status chunk_attention(const skv_cache* cache, const void* q, const void* k_cur, const void* v_cur,
                            int32_t n_frames, void* out, void* stream);
 

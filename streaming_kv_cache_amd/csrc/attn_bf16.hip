@@ -7,31 +7,34 @@
 // chunk, so no mask is needed inside a range).  Tiles never cross a range, so
 // only the last tile of each range is partial.
 //
-// Two kernels share the score / softmax / output code path:
+// Two kernels:
 //   * attn_bf16_vt_kernel (the cache path): V arrives transposed (V^T[h][d][key],
-//     the layout the V store keeps), K and V^T tiles are moved global -> LDS with
-//     direct-to-LDS loads into XOR-swizzled layouts, 4 waves x 32 query rows per
-//     workgroup, two workgroups per CU (two waves per SIMD, so one wave's softmax
-//     overlaps the other's matrix work);
+//     the layout the V store keeps); K rows and V^T tiles go global -> LDS with
+//     direct-to-LDS buffer loads into padded, conflict-free layouts.  Two shapes:
+//     4 waves x 32 query rows with two stages (two workgroups per CU), or 8 waves
+//     x 32 rows with four stages (one workgroup per CU); the host picks the one
+//     that needs fewer dispatch rounds;
 //   * attn_bf16_tokv_kernel (cross attention over caller-provided token-major V):
 //     tiles staged through registers, V transposed on its way into LDS.
 //
 // Work decomposition (wave64, gfx950):
-//   * a workgroup owns BM = NW*32*QB query rows of one head; each wave owns
-//     32*QB rows; workgroup ids are remapped so that the workgroups one XCD runs
-//     work on consecutive tiles of the same head (they share K/V in that XCD's L2);
-//   * the key loop walks tiles of 64 keys; K rows and V^T are staged in LDS
-//     (double-buffered, loads for tile t+1 in flight while tile t is computed);
+//   * a workgroup owns the query rows of its waves for one head; workgroup ids are
+//     remapped so that the workgroups one XCD runs work on consecutive tiles of
+//     the same head (they share K/V in that XCD's L2);
+//   * the key loop walks tiles of 64 keys, loads running one or two tiles ahead;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q^T kept in
 //     registers), so each lane holds scores of ONE query: row max and row sum
 //     need a single cross-lane step (lanes l and l^32);
 //   * the K rows feeding the A operand are read in an order that swaps bits 2
 //     and 3 of the row index, which makes the score registers come out in the
 //     key order the P^T B operand of the second product needs;
-//   * O^T += V^T P^T with P rounded to bf16; online softmax in fp32 with exp2,
-//     rescaling the accumulators only when the running max grows by more than
-//     2^8 (the result is the same; P stays below 256);
+//   * O^T += V^T P^T with P rounded to bf16; softmax in fp32 with exp2 against a
+//     running max that is raised only when a row sum would pass 2^60 (the result
+//     is the same for any max); each 64-key tile is done in two 32-key halves so
+//     the exponentials of one half overlap the matrix products of the other;
 //   * deterministic: no atomics, fixed reduction order.
+#include <cstdlib>
+
 #include "skv_device.hpp"
 #include "skv_kernels.hpp"
 
@@ -328,7 +331,7 @@ hipError_t launch_attention_bf16_tokv(const AttnArgs& a, int D, hipStream_t stre
 }  // namespace skv
 
 // ============================================================================
-// Cache-path kernel: transposed V, direct-to-LDS tiles, two workgroups per CU.
+// Cache-path kernel: transposed V, direct-to-LDS tiles, NW waves, NSTAGE tile stages.
 // ============================================================================
 namespace skv {
 
@@ -340,13 +343,37 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void*
 
 }  // namespace
 
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// 16 bytes per lane from base + voff + soff straight into LDS (lane l writes lds + 16 l).
+// A buffer load rather than a global one: the compiler then tracks it as a plain vector-memory
+// load, and LDS reads issued after it keep their partial lgkmcnt waits.  Offsets stay below 2^31
+// (the host checks the ranges).
+__device__ __forceinline__ void buf_lds16(const void* base, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kRsrcWord3),
+                                           lds_ptr(lds), 16, voff, soff, 0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight and all LDS
+// operations are done, then barrier.  Written out because a fenced barrier also waits
+// for the direct-to-LDS loads that are meant to stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  // s_waitcnt fields (gfx9): vmcnt [3:0] and [15:14], expcnt [6:4] (7 = no wait), lgkmcnt [11:8]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+}
+
 // Cross-half (lanes l and l^32) reductions.
 __device__ __forceinline__ float half_swap_max(float x) { return fmaxf(x, xor32(x)); }
 __device__ __forceinline__ float half_swap_sum(float x) { return x + xor32(x); }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
-  constexpr int NW = 4, BM = 128;
+template <int D, int NW, int NSTAGE>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(AttnArgs a) {
+  static_assert(NSTAGE == 2 || NSTAGE == 4, "two or four stages");
+  constexpr int BM = NW * 32;
   constexpr int KP = 2 * D + 16;          // LDS pitch of a K row (bytes): data + one 16-byte pad
   constexpr int VP = 2 * kBN + 16;        // LDS pitch of a V^T row (64 keys + pad)
   constexpr int KT_B = kBN * KP, VT_B = D * VP;
@@ -355,12 +382,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
   constexpr int KCPR = 2 * D / 16;        // data chunks per K row
   constexpr int KSTEPS = D / 16, MBLK = D / 32;
   static_assert(KT_B % 1024 == 0 && VT_B % 1024 == 0, "tiles must be whole 1-KB blocks");
-  // [K stage 0 | K stage 1 | V^T stage 0 | V^T stage 1].  A padded pitch of 68 (K) or 36 (V^T)
+  // fewest direct loads any wave issues per K / V^T tile: the in-order vmcnt thresholds
+  constexpr int KMIN = KBLK / NW, VMIN = VBLK / NW;
+  // [K stages | V^T stages].  A padded pitch of 68 (K) or 36 (V^T)
   // dwords puts the 16 rows a 16-lane group reads on 16 distinct 4-bank groups, so both
   // products read conflict-free with addresses that are a lane constant plus an immediate.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KT_B + 2 * VT_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * (KT_B + VT_B)];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
   const int l32 = lane & 31, hf = lane >> 5;
   const int n_qt = (a.Lq + BM - 1) / BM;
   const int tile = xcd_remap(blockIdx.x, n_qt * a.H);
@@ -388,29 +418,24 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
   float m_run = 0.f, l_run = 0.f;
-  f32x16_t negm;  // -m_run in every entry: the accumulator the score product starts from
-#pragma unroll
-  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
 
-  // Lane-constant parts of the direct loads.  Lane l of block blk fills LDS bytes
-  // [blk*1024 + 16 l, +16); lanes that land on a pad chunk fetch a harmless valid chunk.
-  int kq_row[KI], kq_c16[KI], vq_row[VI], vq_chk[VI];
-#pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    const int ob = (wave + NW * i) * 1024 + 16 * lane;
-    int row = ob / KP, ch = (ob % KP) / 16;
-    if (ch >= KCPR || row >= kBN) row = 0, ch = 0;
-    kq_row[i] = row;
-    kq_c16[i] = 16 * ch;
-  }
-#pragma unroll
-  for (int i = 0; i < VI; ++i) {
-    const int ob = (wave + NW * i) * 1024 + 16 * lane;
-    int d = ob / VP, ch = (ob % VP) / 16;
+  // Lane part of the direct loads.  Lane l of block blk fills LDS bytes [blk*1024 + 16 l, +16);
+  // lanes that land on a pad chunk fetch a harmless valid chunk (row 0, chunk 0).
+  // `ln` is the lane id passed through an empty asm so that the partial-tile paths recompute
+  // their offsets instead of keeping them live in registers across the loop.
+  auto k_lane = [&](int i, int ln, int& row, int& c16) {
+    const int ob = (wave + NW * i) * 1024 + 16 * ln;
+    row = ob / KP;
+    const int ch = (ob % KP) / 16;
+    if (ch >= KCPR || row >= kBN) row = 0, c16 = 0; else c16 = 16 * ch;
+  };
+  auto v_lane = [&](int i, int ln, int& d, int& ch) {
+    const int ob = (wave + NW * i) * 1024 + 16 * ln;
+    d = ob / VP;
+    ch = (ob % VP) / 16;
     if (ch >= 8 || d >= D) d = 0, ch = 0;
-    vq_row[i] = d;
-    vq_chk[i] = ch;
-  }
+  };
+  int kq_off[KI], vq_off[VI];  // byte offsets for whole tiles of the current range
 
   // Two uniform tile iterators over the key ranges: K runs ahead of V.
   int n_tiles = 0;
@@ -418,20 +443,38 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
   if (n_tiles == 0) return;  // no keys: the host never launches this
   int ksi = 0, krem = 0, k_rs_b = 0;
   const uint8_t* kp = nullptr;
+  
+  int k_so = 0;
   auto k_seg = [&](int s_) {
     const KvSeg sg = a.seg[s_];
     kp = (const uint8_t*)sg.k + 2 * (int64_t)h * sg.k_hs;
+    k_so = 0;
     k_rs_b = (int)(2 * sg.k_rs);
     krem = sg.n;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      int row, c16;
+      k_lane(i, lane, row, c16);
+      kq_off[i] = row * k_rs_b + c16;
+    }
   };
   int vsi = 0, vrem = 0, v_ds_b = 0, v_al16 = 1;
   const uint8_t* vp = nullptr;
+  
+  int v_so = 0;
   auto v_seg = [&](int s_) {
     const KvSeg sg = a.seg[s_];
     vp = (const uint8_t*)sg.v + 2 * (int64_t)h * sg.v_hs;
+    v_so = 0;
     v_ds_b = (int)(2 * sg.v_ds);
     vrem = sg.n;
     v_al16 = sg.v_al16;
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      int d, ch;
+      v_lane(i, lane, d, ch);
+      vq_off[i] = d * v_ds_b + 16 * ch;
+    }
   };
   k_seg(0);
   while (krem <= 0 && ++ksi < a.nseg) k_seg(ksi);
@@ -442,32 +485,53 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
   auto issue_k = [&](int st) -> int {
     const int nk = krem < kBN ? krem : kBN;
     uint8_t* dst = smem + st * KT_B;
+    if (nk == kBN) {
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int blk = wave + NW * i;
-      if (blk < KBLK) {
-        const int rr = kq_row[i] < nk ? kq_row[i] : 0;  // rows past the range: a valid row (masked)
-        __builtin_amdgcn_global_load_lds(kp + (uint32_t)(rr * k_rs_b + kq_c16[i]), lds_ptr(dst + blk * 1024), 16, 0,
-                                         0);
+      for (int i = 0; i < KI; ++i) {
+        const int blk = wave + NW * i;
+        if (blk < KBLK) buf_lds16(kp - k_so, dst + blk * 1024, kq_off[i], k_so);
+      }
+    } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const int blk = wave + NW * i;
+        if (blk < KBLK) {
+          int row, c16;
+          k_lane(i, ln, row, c16);
+          const int rr = row < nk ? row : 0;  // rows past the range: a valid row (masked)
+          buf_lds16(kp - k_so, dst + blk * 1024, rr * k_rs_b + c16, k_so);
+        }
       }
     }
     krem -= kBN;
     kp += kBN * k_rs_b;
+    k_so += kBN * k_rs_b;
     while (krem <= 0 && ++ksi < a.nseg) k_seg(ksi);
     return nk;
   };
   // Issue the next V^T tile into stage st.
   auto issue_v = [&](int st) {
     const int nk = vrem < kBN ? vrem : kBN;
-    uint8_t* dst = smem + 2 * KT_B + st * VT_B;
-    if (v_al16) {
+    uint8_t* dst = smem + NSTAGE * KT_B + st * VT_B;
+    if (v_al16 && nk == kBN) {
+#pragma unroll
+      for (int i = 0; i < VI; ++i) {
+        const int blk = wave + NW * i;
+        if (blk < VBLK) buf_lds16(vp - v_so, dst + blk * 1024, vq_off[i], v_so);
+      }
+    } else if (v_al16) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int i = 0; i < VI; ++i) {
         const int blk = wave + NW * i;
         if (blk < VBLK) {
-          const int cc = 8 * vq_chk[i] < nk ? vq_chk[i] : 0;  // chunks past the range: valid data, P is 0
-          __builtin_amdgcn_global_load_lds(vp + (uint32_t)(vq_row[i] * v_ds_b + 16 * cc),
-                                           lds_ptr(dst + blk * 1024), 16, 0, 0);
+          int d, ch;
+          v_lane(i, ln, d, ch);
+          const int cc = 8 * ch < nk ? ch : 0;  // chunks past the range: valid data, P is 0
+          buf_lds16(vp - v_so, dst + blk * 1024, d * v_ds_b + 16 * cc, v_so);
         }
       }
     } else {
@@ -480,6 +544,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
     }
     vrem -= kBN;
     vp += 2 * kBN;
+    v_so += 2 * kBN;
     while (vrem <= 0 && ++vsi < a.nseg) v_seg(vsi);
   };
 
@@ -490,114 +555,185 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
   const int voff = l32 * VP + 16 * hf;
   const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  // prologue: K0, V0, K1 in flight
-  int nk_k[2];
-  nk_k[0] = issue_k(0);
-  issue_v(0);
-  if (n_tiles > 1) nk_k[1] = issue_k(1);
+  // Two stages: K runs one half-tile ahead of V (K0, V0, K1 in flight at the start), two
+  // barriers per tile.  Four stages: whole tiles NSTAGE-2 ahead, one barrier per tile.
+  int nk_k[2] = {0, 0};      // two stages: valid keys of the K tile in each stage
+  int nkq[3] = {0, 0, 0};    // four stages: valid keys of the next tiles, oldest first
+  if constexpr (NSTAGE == 2) {
+    nk_k[0] = issue_k(0);
+    issue_v(0);
+    if (n_tiles > 1) nk_k[1] = issue_k(1);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i)
+      if (i < n_tiles) {
+        nkq[i] = issue_k(i);
+        issue_v(i);
+      }
+  }
+
+  // P = exp2(S' - m_run) for one 32-key half, packed to bf16 in B-operand order; returns the
+  // row sum of the rounded values.
+  auto exp_half = [&](const f32x16_t& sv, bf16x8_t& p0, bf16x8_t& p1) -> float {
+    float ls = 0.f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4_t pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * half + 2 * e;
+        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sv[r] - m_run), __builtin_amdgcn_exp2f(sv[r + 1] - m_run));
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, one2), ls,
+                                             false);
+        pk[e] = w;
+      }
+      (half ? p1 : p0) = __builtin_bit_cast(bf16x8_t, pk);
+    }
+    return ls;
+  };
+  auto max_half = [&](const f32x16_t& sv) -> float {
+    float ma = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) ma = fmaxf(fmaxf(ma, sv[r]), sv[r + 1]);
+    return half_swap_max(fmaxf(ma, sv[15]));
+  };
+  // Raise the running max by up: rescale what has been accumulated.
+  auto raise_by = [&](float up) {
+    const float alpha = __builtin_amdgcn_exp2f(-up);
+    l_run *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+    m_run += up;
+  };
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
+    const int st = NSTAGE == 2 ? (t & 1) : (t & 3);
     const bool more = t + 1 < n_tiles;
-    // K_t landed (V_t and K_{t+1} may still be in flight), then everyone's V_{t-1} reads are done.
-    // Explicit waits + barrier: a fenced barrier would also wait for the loads still in flight.
-    if (more)
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (more) issue_v(st ^ 1);
+    int nk;
+    if constexpr (NSTAGE == 2) {
+      // K_t landed (V_t and K_{t+1} may still be in flight), then everyone's V_{t-1} reads are done.
+      if (more)
+        wait_vm_barrier<KMIN + VMIN>();
+      else
+        wait_vm_barrier<VMIN>();
+      if (more) issue_v(st ^ 1);
+      nk = nk_k[st];
+    } else {
+      // tile t landed (up to two later tiles may still be in flight), then everyone is done
+      // with tile t-1, whose stage takes tile t+3
+      if (t + 2 < n_tiles)
+        wait_vm_barrier<2 * (KMIN + VMIN)>();
+      else if (more)
+        wait_vm_barrier<KMIN + VMIN>();
+      else
+        wait_vm_barrier<0>();
+      nk = nkq[0];
+      nkq[0] = nkq[1];
+      nkq[1] = nkq[2];
+      if (t + NSTAGE - 1 < n_tiles) {
+        const int sn = (t + NSTAGE - 1) & 3;
+        nkq[2] = issue_k(sn);
+        issue_v(sn);
+      }
+    }
 
-    // ---- S'^T = K (Q^T * scale * log2 e) - m_run
     const uint8_t* kt = smem + st * KT_B;
-    f32x16_t s0 = negm, s1 = negm;
+    // ---- keys 0..31: S'^T = K (Q^T * scale * log2 e)
+    // all LDS reads of a product are issued before its first MFMA (sched_barrier keeps them there)
+    bf16x8_t ka[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8_t a0 = ld_bf16x8(kt + koff[0] + 32 * ks);
-      const bf16x8_t a1 = ld_bf16x8(kt + koff[1] + 32 * ks);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
+    for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = ld_bf16x8(kt + koff[0] + 32 * ks);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16_t s0 = {};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s0, 0, 0, 0);
+    if (nk < 32) {
+      int nkh = nk - 8 * hf;  // key score_key(r, hf) >= nk  <=>  score_key(r, 0) >= nk - 8 hf
+      asm volatile("" : "+v"(nkh));
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (score_key(r, 0) >= nkh) s0[r] = -INFINITY;
     }
-    const int nk = nk_k[st];
-    if (nk < kBN) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (score_key(r, hf) >= nk) s0[r] = -INFINITY;
-        if (32 + score_key(r, hf) >= nk) s1[r] = -INFINITY;
-      }
+    if (t == 0) {
+      // first tile: the running max starts at the max of its first half (key 0 is always valid)
+      m_run = max_half(s0);
     }
 
-    // ---- P = exp2(S'), packed to bf16 in the B-operand order; row sums of the bf16 values.
-    // The running max is raised only when some score exceeds it by a lot (first tile, or a
-    // row sum past 2^60): the result is the same for any max, and P stays far below overflow.
+    // ---- keys 32..63 on the matrix cores while P of keys 0..31 is formed
+    f32x16_t s1 = {};
     bf16x8_t pb[4];
-    float lsum = 0.f;
-    auto exp_pack = [&](float sub) {
-      lsum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const f32x16_t& sv = kb ? s1 : s0;
+    for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = ld_bf16x8(kt + koff[1] + 32 * ks);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4_t pk;
+    for (int ks = 0; ks < KSTEPS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s1, 0, 0, 0);
+    float lsum = exp_half(s0, pb[0], pb[1]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 8 * half + 2 * e;
-            const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sv[r] - sub), __builtin_amdgcn_exp2f(sv[r + 1] - sub));
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, one2),
-                                                   lsum, false);
-            pk[e] = w;
-          }
-          pb[2 * kb + half] = __builtin_bit_cast(bf16x8_t, pk);
-        }
-      }
-    };
-    bool raise = t == 0;
-    if (!raise) {
-      exp_pack(0.f);
-      raise = __any(lsum > 0x1p60f);
+    for (int i = 0; i < KSTEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 48 / KSTEPS, 0);
     }
-    if (raise) {
-      float ma = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
-      float mb_ = fmaxf(fmaxf(s1[0], s1[1]), s1[2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) {
-        ma = fmaxf(fmaxf(ma, s0[r]), s0[r + 1]);
-        mb_ = fmaxf(fmaxf(mb_, s1[r]), s1[r + 1]);
-      }
-      float mx = fmaxf(fmaxf(ma, s0[15]), fmaxf(mb_, s1[15]));
-      mx = half_swap_max(mx);
-      // first tile: m_run = max; later: only ever raise it
-      const float up = t == 0 ? mx : fmaxf(mx, 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-up);
-      l_run *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-      m_run += up;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) negm[r] = -m_run;
-      exp_pack(up);
+    // The running max is raised only when some score exceeds it by a lot (a row sum past
+    // 2^60): the result is the same for any max, and P stays far below overflow.
+    if (__any(lsum > 0x1p60f)) {
+      raise_by(fmaxf(max_half(s0) - m_run, 0.f));
+      lsum = exp_half(s0, pb[0], pb[1]);
     }
     l_run += lsum;
-
-    // V_t landed (K_{t+1} and V_{t+1} may still be in flight), then everyone's K_t reads are done
-    if (more)
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 2 < n_tiles) nk_k[st] = issue_k(st);
-
-    // ---- O^T += V^T P^T
-    const uint8_t* vt = smem + 2 * KT_B + st * VT_B;
+    if (nk < kBN) {
+      int nkh = nk - 32 - 8 * hf;
+      asm volatile("" : "+v"(nkh));
 #pragma unroll
-    for (int stp = 0; stp < 4; ++stp) {
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb) {
-        const bf16x8_t av = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[stp], o[mb], 0, 0, 0);
-      }
+      for (int r = 0; r < 16; ++r)
+        if (score_key(r, 0) >= nkh) s1[r] = -INFINITY;
     }
+
+    if constexpr (NSTAGE == 2) {
+      // V_t landed (K_{t+1} and V_{t+1} may still be in flight), then everyone's K_t reads are done
+      if (more)
+        wait_vm_barrier<KMIN + VMIN>();
+      else
+        wait_vm_barrier<0>();
+      if (t + 2 < n_tiles) nk_k[st] = issue_k(st);
+    }
+
+    // ---- O^T += V^T P^T over keys 0..31 while P of keys 32..63 is formed
+    const uint8_t* vt = smem + NSTAGE * KT_B + st * VT_B;
+    bf16x8_t va[2 * MBLK];
+#pragma unroll
+    for (int stp = 0; stp < 2; ++stp)
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb) va[stp * MBLK + mb] = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int stp = 0; stp < 2; ++stp)
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[stp * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
+    lsum = exp_half(s1, pb[2], pb[3]);
+#pragma unroll
+    for (int i = 0; i < 2 * MBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * MBLK), 0);
+    }
+    if (__any(lsum > 0x1p60f)) {
+      raise_by(fmaxf(max_half(s1) - m_run, 0.f));
+      lsum = exp_half(s1, pb[2], pb[3]);
+    }
+    l_run += lsum;
+    // ---- O^T += V^T P^T over keys 32..63
+#pragma unroll
+    for (int stp = 2; stp < 4; ++stp)
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb) va[(stp - 2) * MBLK + mb] = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int stp = 2; stp < 4; ++stp)
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[(stp - 2) * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
   }
 
   const float inv = 1.f / half_swap_sum(l_run);
@@ -615,12 +751,24 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_vt_kernel(AttnArgs a) {
   }
 }
 
+// Two shapes of the same kernel: 4 waves x 32 queries with two stages (two workgroups per CU),
+// or 8 waves x 32 queries with four stages (one workgroup per CU; each K/V tile feeds twice the
+// queries and loads run two tiles ahead).  The larger one runs about 10% faster per query once
+// the grid fills the chip; with few query tiles its coarser grid leaves CUs idle, so pick by
+// the number of dispatch rounds each needs on 256 CUs.
 hipError_t launch_attention_bf16_vt(const AttnArgs& a, int D, hipStream_t stream) {
-  const int n_qt = (a.Lq + 127) / 128;
-  dim3 grid(n_qt * a.H);
-  switch (D) {
-    case 64: hipLaunchKernelGGL(attn_bf16_vt_kernel<64>, grid, dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(attn_bf16_vt_kernel<128>, grid, dim3(256), 0, stream, a); break;
+  const int64_t wg4 = (int64_t)((a.Lq + 127) / 128) * a.H, wg8 = (int64_t)((a.Lq + 255) / 256) * a.H;
+  const double rounds4 = (double)((wg4 + 511) / 512), rounds8 = 0.9 * (double)((wg8 + 255) / 256);
+  // SKV_ATTN_WAVES=4 or 8 forces one shape (tests cover both on small inputs)
+  const char* env = std::getenv("SKV_ATTN_WAVES");
+  const int forced = env ? std::atoi(env) : 0;
+  const bool big = forced == 8 || (forced != 4 && rounds8 < rounds4);
+  const dim3 grid((unsigned)(big ? wg8 : wg4));
+  switch (D * (big ? -1 : 1)) {
+    case 64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 4, 2>), grid, dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 4, 2>), grid, dim3(256), 0, stream, a); break;
+    case -64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 8, 4>), grid, dim3(512), 0, stream, a); break;
+    case -128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 8, 4>), grid, dim3(512), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -33,6 +33,15 @@ skv_status make_geometry(const skv_config* cfg, Geometry* g) {
   r.dtype = cfg->dtype;
   r.elt = r.dtype == SKV_BF16 ? 2 : 4;
   if (!attention_head_dim_supported(r.dtype, r.D)) return SKV_ERR_CONFIG;
+  if (r.dtype == SKV_BF16) {
+    // the bf16 attention kernel addresses each head's key range with 32-bit byte offsets:
+    // the current chunk (token-major rows of H*D), the stores' rows, and V^T rows of W*F keys
+    const int64_t lim = INT32_MAX;
+    const int64_t cur = ((int64_t)r.c * r.F + 64) * r.H * r.D * r.elt;
+    const int64_t kst = ((int64_t)r.W * r.F + 64) * r.D * r.elt;
+    const int64_t vst = (int64_t)r.D * ((int64_t)r.W * r.F + 64) * r.elt;
+    if (cur > lim || kst > lim || vst > lim) return SKV_ERR_CONFIG;
+  }
   if (cfg->rope_mode != SKV_ROPE_ABS && cfg->rope_mode != SKV_ROPE_REL) return SKV_ERR_CONFIG;
   r.mode = cfg->rope_mode;
   if (cfg->rope_t == 0 && cfg->rope_h == 0 && cfg->rope_w == 0) {

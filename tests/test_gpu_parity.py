@@ -153,6 +153,18 @@ def test_rollout_parity(name):
     say(f"  worst max/mean/relrms = {worst}")
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("name", ["small_abs", "small_rel", "small_d64", "small_nosink"])
+def test_rollout_parity_kernel_shapes(name, waves, monkeypatch):
+    """Both bf16 kernel shapes (4 waves / two stages, 8 waves / four stages) on the same rollouts."""
+    monkeypatch.setenv("SKV_ATTN_WAVES", waves)
+    wl = WORKLOADS[name]
+    say(f"[rollout] {name} waves={waves} chunks={wl.n_chunks}")
+    for ch, p, out, ref in ro.rollout(wl, wl.n_chunks):
+        torch.cuda.synchronize()
+        ro.assert_close(out, ref, wl.cfg.dtype, f"{name} waves {waves} chunk {ch} pass {p}")
+
+
 def _probe_rollout(wl, mode):
     """q = 0 with one-hot (mode 'onehot') or random (mode 'zeroq') values: the answer is a plain mean."""
     c = wl.cfg
