@@ -70,7 +70,8 @@ class Runner:
             for p in range(wl.passes):
                 qkv = [si.draw(shape, 0, sidx, p, tid, dt) for tid in (si.Q, si.K, si.V)]
                 passes_cpu.append(qkv)
-                passes_dev.append([x.cuda() for x in qkv])
+                # the sampler's noise for this pass (pass 0: the chunk's starting latent)
+                passes_dev.append([x.cuda() for x in qkv] + [si.draw(shape, 0, sidx, p, si.NOISE, dt).cuda()])
             self.cpu_pool.append(passes_cpu)
             self.pool.append(passes_dev)
         if wl.text_tokens:
@@ -80,6 +81,10 @@ class Runner:
         self.qr = torch.empty(shape, dtype=dt, device="cuda")
         self.kr = [torch.empty(shape, dtype=dt, device="cuda") for _ in range(wl.layers)]
         self.out = torch.empty(shape, dtype=dt, device="cuda")
+        # the chunk's latent and its clean estimate for the sampler between passes; the last
+        # layer's attention output stands in for the velocity the forward would predict
+        self.x = torch.empty(shape, dtype=dt, device="cuda")
+        self.x0 = torch.empty(shape, dtype=dt, device="cuda")
         self.chunk = 0
         self.ev = None
 
@@ -110,8 +115,9 @@ class Runner:
             for cache in self.caches:
                 cache.rope_apply_window()
             self._ev("win1")
+        steps = wl.timesteps
         for p in range(wl.passes):
-            q, k, v = sets[p]
+            q, k, v, noise = sets[p]
             for li, cache in enumerate(self.caches):
                 t = cache.info().n_appended
                 self._ev("rope0")
@@ -131,12 +137,20 @@ class Runner:
                     self._ev("app0")
                     cache.append_evict(k if self.rel else self.kr[li], v)
                     self._ev("app1")
+            if p < len(steps):
+                # few-step sampler: x0 from the velocity; re-noise to the next step unless last
+                last = p + 1 == len(steps)
+                self._ev("samp0")
+                self.skv.sampler_step(sets[0][3] if p == 0 else self.x, self.out, steps[p] / 1000.0,
+                                      0.0 if last else steps[p + 1] / 1000.0, noise=None if last else noise,
+                                      x0_out=self.x0, x_next_out=None if last else self.x)
+                self._ev("samp1")
         self._ev("step1")
         self.chunk += 1
 
     def fill_step(self):
         """Advance the cache by one chunk (write-back only): builds the steady state without attention."""
-        _, k, v = self.pool[self.chunk % len(self.pool)][self.wl.passes - 1]
+        _, k, v, _ = self.pool[self.chunk % len(self.pool)][self.wl.passes - 1]
         for li, cache in enumerate(self.caches):
             kk = k if self.rel else cache.rope_apply(k, out=self.kr[li], start_frame=cache.info().n_appended)
             cache.append_evict(kk, v)
@@ -231,7 +245,7 @@ def main():
         r.step()
     torch.cuda.synchronize()
     r.ev = {k: [] for k in ("step0", "step1", "win0", "win1", "rope0", "rope1", "stage0", "attn0", "attn1",
-                            "cross0", "cross1", "app0", "app1")}
+                            "cross0", "cross1", "app0", "app1", "samp0", "samp1")}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -249,6 +263,7 @@ def main():
     rope_ms, _ = avg_ms(ev, "rope0", "rope1")
     win_ms, _ = avg_ms(ev, "win0", "win1")
     cross_ms, _ = avg_ms(ev, "cross0", "cross1")
+    samp_ms, _ = avg_ms(ev, "samp0", "samp1")
     _, steps_ms = avg_ms(ev, "step0", "step1")
 
     c, f, h, d = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim
@@ -289,6 +304,12 @@ def main():
         "per_chunk_ms": {"mean": round(float(np.mean(steps_ms)), 4), "p50": round(float(np.median(steps_ms)), 4),
                          "p99": round(float(np.percentile(steps_ms, 99)), 4)},
     }
+    if wl.timesteps:
+        # per call: x_t, velocity and noise read, x0 and the re-noised latent written (last step: x0 only)
+        ns = len(wl.timesteps)
+        samp_bytes = ((ns - 1) * 5 + 3) / ns * lq * h * d * elt
+        out["sampler"] = {"GB/s": round(samp_bytes / (samp_ms * 1e-3) / 1e9, 1), "avg_us": round(samp_ms * 1e3, 2),
+                          "timesteps": list(wl.timesteps)}
     if r.rel:
         win_bytes = 2 * (cfg.window_frames - c) * f * h * d * elt
         out["rope_window"] = {"GB/s": round(win_bytes / (win_ms * 1e-3) / 1e9, 1), "avg_us": round(win_ms * 1e3, 2)}

@@ -172,6 +172,27 @@ skv_status kv_cache_info(const skv_cache* cache, kv_cache_info_t* info);
 skv_status kv_cache_gather(const skv_cache* cache, void* k_out, void* v_out, int64_t* frame_ids_host,
                            void* stream);
 
+/* One step of the few-step sampler between attention passes ([LB-fast]
+ * "2. 4 步采样": the forward gives a flow-matching velocity, x0 is recovered in
+ * one step and re-noised to the next, smaller timestep unless it was the last;
+ * the conversion runs in double precision).  Element-wise over n elements of
+ * dtype (any layout):
+ *   v      = v_cond, or v_uncond + cfg_scale * (v_cond - v_uncond) when
+ *            v_uncond is not NULL (guidance of the causal_pretrain mode);
+ *   x0     = x_t - sigma * v                       -> x0_out (if not NULL);
+ *   x_next = (1 - sigma_next) * x0 + sigma_next * noise -> x_next_out (if not NULL;
+ *            needs noise).
+ * Arithmetic in fp64, results rounded to dtype (bf16: to fp32, then to bf16,
+ * each to nearest even).  Outputs may alias x_t (each element is read before it
+ * is written).  sigma for timestep t of 1000 training steps is t / 1000 in the
+ * schedules the tests use; the call takes the sigmas themselves.
+ * Errors: NULL x_t / v_cond, both outputs NULL, or x_next_out without noise ->
+ * SKV_ERR_NULL; misaligned pointer -> SKV_ERR_ALIGN; bad dtype or non-finite
+ * scalar -> SKV_ERR_CONFIG; n < 0 -> SKV_ERR_SHAPE; n == 0 enqueues nothing. */
+skv_status sampler_step(const void* x_t, const void* v_cond, const void* v_uncond, double cfg_scale,
+                        const void* noise, int64_t n, double sigma, double sigma_next, int32_t dtype,
+                        void* x0_out, void* x_next_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

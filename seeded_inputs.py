@@ -14,8 +14,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-# tensor ids inside one (chunk, pass) draw
-Q, K, V, TEXT_K, TEXT_V, SINK_K, SINK_V = 0, 1, 2, 3, 4, 5, 6
+# tensor ids inside one (chunk, pass) draw (NOISE: the sampler's fresh noise / starting latent)
+Q, K, V, TEXT_K, TEXT_V, SINK_K, SINK_V, NOISE = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def seed_for(base: int, chunk: int, pass_idx: int, tensor_id: int) -> int:

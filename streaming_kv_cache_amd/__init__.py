@@ -24,7 +24,7 @@ ROPE_ABS, ROPE_REL = 0, 1
 EXPORTED = (
     "skv_abi_version", "skv_status_string", "kv_cache_bytes", "kv_cache_init", "kv_cache_reset",
     "kv_cache_destroy", "kv_cache_append_evict", "rope_apply", "rope_apply_window", "chunk_attention",
-    "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v",
+    "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v", "sampler_step",
 )
 
 
@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
         "kv_cache_info": ([vp, ctypes.POINTER(KvCacheInfo)], st),
         "kv_cache_gather": ([vp, vp, vp, ctypes.POINTER(ctypes.c_int64), vp], st),
         "kv_cache_stage_v": ([vp, vp, i32, vp], st),
+        "sampler_step": ([vp, vp, vp, ctypes.c_double, vp, i64, ctypes.c_double, ctypes.c_double, i32, vp, vp, vp],
+                         st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -251,3 +253,22 @@ def cross_attention(q: torch.Tensor, k_text: torch.Tensor, v_text: torch.Tensor,
     _check(lib.cross_attention(_ptr(q), q.shape[0], _ptr(k_text), _ptr(v_text), k_text.shape[0], q.shape[1],
                                q.shape[2], _dtype_code(q.dtype), _ptr(out), _stream(stream)), "cross_attention")
     return out
+
+
+def sampler_step(x_t: torch.Tensor, v_cond: torch.Tensor, sigma: float, sigma_next: float = 0.0,
+                 noise: Optional[torch.Tensor] = None, v_uncond: Optional[torch.Tensor] = None,
+                 cfg_scale: float = 1.0, x0_out: Optional[torch.Tensor] = None,
+                 x_next_out: Optional[torch.Tensor] = None, want_x0: bool = True, stream=None):
+    """One sampler step (see ``sampler_step`` in skv.h).  Returns (x0, x_next); x_next is None without noise."""
+    ts = [t for t in (x_t, v_cond, v_uncond, noise, x0_out, x_next_out) if t is not None]
+    for t in ts:
+        if t.dtype != x_t.dtype or t.numel() != x_t.numel() or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("contiguous CUDA tensors of one dtype and size expected")
+    if want_x0 and x0_out is None:
+        x0_out = torch.empty_like(x_t)
+    if noise is not None and x_next_out is None:
+        x_next_out = torch.empty_like(x_t)
+    _check(lib.sampler_step(_ptr(x_t), _ptr(v_cond), _ptr(v_uncond), float(cfg_scale), _ptr(noise), x_t.numel(),
+                            float(sigma), float(sigma_next), _dtype_code(x_t.dtype), _ptr(x0_out),
+                            _ptr(x_next_out), _stream(stream)), "sampler_step")
+    return x0_out, x_next_out

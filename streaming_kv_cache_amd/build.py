@@ -23,7 +23,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["skv_core.cpp", "skv_lib.cpp", "cache_kernels.hip", "vt_kernels.hip", "attn_f32.hip", "attn_bf16.hip"]
+SOURCES = ["skv_core.cpp", "skv_lib.cpp", "cache_kernels.hip", "vt_kernels.hip", "attn_f32.hip", "attn_bf16.hip", "sampler_kernels.hip"]
 
 
 def hipcc() -> str:

@@ -1,0 +1,95 @@
+// Few-step sampler glue between attention passes (gfx950): flow-matching velocity
+// -> clean latent -> re-noised latent at the next timestep, element-wise.
+// [LB-fast] "2. 4 步采样": x0 is recovered from x_t, sigma_t and the velocity in one
+// step and re-noised to the next, smaller timestep unless it was the last one; the
+// conversion runs in double precision (the page's precision remark).  Guidance, when
+// asked for, mixes two velocity predictions first (the causal_pretrain mode's CFG).
+// HBM-bound: each thread moves 16 bytes of every operand per iteration.
+#include "skv_device.hpp"
+#include "skv_kernels.hpp"
+
+namespace skv {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ double to_f64(float x) { return (double)x; }
+__device__ __forceinline__ double to_f64(uint16_t b) { return (double)__uint_as_float((uint32_t)b << 16); }
+
+template <typename T>
+__device__ __forceinline__ T from_f64(double x);
+template <>
+__device__ __forceinline__ float from_f64<float>(double x) {
+  return (float)x;  // round to nearest even
+}
+template <>
+__device__ __forceinline__ uint16_t from_f64<uint16_t>(double x) {
+  return (uint16_t)(pack_bf16x2((float)x, 0.f) & 0xffffu);  // to fp32, then to bf16, each rounding to nearest even
+}
+
+template <typename T>
+__device__ __forceinline__ void step_one(const SamplerArgs& a, int64_t i) {
+  const double x = to_f64(((const T*)a.x_t)[i]);
+  double v = to_f64(((const T*)a.v_cond)[i]);
+  if (a.v_uncond) {
+    const double vu = to_f64(((const T*)a.v_uncond)[i]);
+    v = vu + a.cfg_scale * (v - vu);
+  }
+  const double x0 = x - a.sigma * v;
+  if (a.x0_out) ((T*)a.x0_out)[i] = from_f64<T>(x0);
+  if (a.x_next_out) {
+    const double e = to_f64(((const T*)a.noise)[i]);
+    ((T*)a.x_next_out)[i] = from_f64<T>((1.0 - a.sigma_next) * x0 + a.sigma_next * e);
+  }
+}
+
+}  // namespace
+
+// grid-stride over 16-byte vectors; the tail (n not a multiple of the vector) element by element.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sampler_kernel(SamplerArgs a) {
+  constexpr int P = 16 / sizeof(T);
+  const int64_t nvec = a.n / P;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t vi = (int64_t)blockIdx.x * kThreads + threadIdx.x; vi < nvec; vi += stride) {
+    const u32x4_t xr = ((const u32x4_t*)a.x_t)[vi];
+    const u32x4_t vcr = ((const u32x4_t*)a.v_cond)[vi];
+    const u32x4_t vur = a.v_uncond ? ((const u32x4_t*)a.v_uncond)[vi] : u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t er = a.x_next_out ? ((const u32x4_t*)a.noise)[vi] : u32x4_t{0u, 0u, 0u, 0u};
+    const T* xs = (const T*)&xr;
+    const T* vcs = (const T*)&vcr;
+    const T* vus = (const T*)&vur;
+    const T* es = (const T*)&er;
+    T x0v[P], xnv[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      double v = to_f64(vcs[e]);
+      if (a.v_uncond) {
+        const double vu = to_f64(vus[e]);
+        v = vu + a.cfg_scale * (v - vu);
+      }
+      const double x0 = to_f64(xs[e]) - a.sigma * v;
+      x0v[e] = from_f64<T>(x0);
+      xnv[e] = from_f64<T>((1.0 - a.sigma_next) * x0 + a.sigma_next * to_f64(es[e]));
+    }
+    if (a.x0_out) ((u32x4_t*)a.x0_out)[vi] = __builtin_bit_cast(u32x4_t, x0v);
+    if (a.x_next_out) ((u32x4_t*)a.x_next_out)[vi] = __builtin_bit_cast(u32x4_t, xnv);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < a.n - nvec * P) step_one<T>(a, nvec * P + threadIdx.x);
+}
+
+hipError_t launch_sampler(const SamplerArgs& a, int elt, hipStream_t stream) {
+  const int P = 16 / elt;
+  const int64_t nvec = a.n / P;
+  int64_t blocks = (nvec + kThreads - 1) / kThreads;
+  if (blocks > 2048) blocks = 2048;  // grid-stride beyond 8 workgroups per CU
+  if (blocks < 1) blocks = 1;
+  if (elt == 2)
+    hipLaunchKernelGGL(sampler_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(sampler_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace skv

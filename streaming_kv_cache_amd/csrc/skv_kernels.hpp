@@ -32,6 +32,18 @@ struct WriteArgs {
   int32_t row_pad;
 };
 hipError_t launch_write_kv(const WriteArgs& a, int elt, hipStream_t stream);
+
+struct SamplerArgs {
+  const void* x_t;
+  const void* v_cond;
+  const void* v_uncond;  // NULL: no guidance
+  const void* noise;     // read only when x_next_out is set
+  void* x0_out;          // NULL: not written
+  void* x_next_out;      // NULL: not written (last step)
+  int64_t n;
+  double cfg_scale, sigma, sigma_next;
+};
+hipError_t launch_sampler(const SamplerArgs& a, int elt, hipStream_t stream);
 hipError_t launch_vt_to_tok(const WriteArgs& a, int elt, hipStream_t stream);
 
 struct RopeLaunch {

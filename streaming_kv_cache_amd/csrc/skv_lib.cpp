@@ -380,6 +380,27 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
   return e == hipSuccess ? SKV_OK : SKV_ERR_HIP;
 }
 
+skv_status sampler_step(const void* x_t, const void* v_cond, const void* v_uncond, double cfg_scale,
+                        const void* noise, int64_t n, double sigma, double sigma_next, int32_t dtype, void* x0_out,
+                        void* x_next_out, void* stream) {
+  skv_status st;
+  if ((st = check_ptr(x_t)) != SKV_OK) return st;
+  if ((st = check_ptr(v_cond)) != SKV_OK) return st;
+  if (!x0_out && !x_next_out) return SKV_ERR_NULL;
+  if (x_next_out && !noise) return SKV_ERR_NULL;
+  const void* opt[4] = {v_uncond, noise, x0_out, x_next_out};
+  for (const void* q : opt)
+    if (q && ((uintptr_t)q & 15)) return SKV_ERR_ALIGN;
+  if (dtype != SKV_F32 && dtype != SKV_BF16) return SKV_ERR_CONFIG;
+  if (!std::isfinite(cfg_scale) || !std::isfinite(sigma) || !std::isfinite(sigma_next)) return SKV_ERR_CONFIG;
+  if (n < 0) return SKV_ERR_SHAPE;
+  if (n == 0) return SKV_OK;
+  skv::SamplerArgs a{x_t, v_cond, v_uncond, x_next_out ? noise : nullptr, x0_out, x_next_out, n,
+                     cfg_scale, sigma, sigma_next};
+  return skv::launch_sampler(a, dtype == SKV_BF16 ? 2 : 4, (hipStream_t)stream) == hipSuccess ? SKV_OK
+                                                                                             : SKV_ERR_HIP;
+}
+
 skv_status kv_cache_gather(const skv_cache* cc, void* k_out, void* v_out, int64_t* frame_ids_host, void* stream) {
   skv_cache* c = const_cast<skv_cache*>(cc);
   skv_status st = check_handle(c);

@@ -24,6 +24,9 @@ class Workload:
     text_tokens: int = 0    # cross-attention keys (0: none)
     layers: int = 1
     steady_chunk: int = 0   # first chunk whose visible set is the full window
+    # timesteps (of 1000 training steps) of the denoise passes; the sampler runs after each
+    # of them with sigma = t / 1000 (the write-back pass runs at t = 0 and is not sampled)
+    timesteps: tuple = ()
 
     @property
     def lq(self) -> int:
@@ -34,19 +37,26 @@ class Workload:
         return self.cfg.window_frames * self.cfg.tokens_per_frame
 
 
+# [ABot-stream] 机制二: denoising_step_list.  [LB-fast] 2. 4 步采样: indices 0, 179, 358, 679 into the
+# 1000-step training table, read as the descending table 1000, 999, ..., 1.
+ABOT_STEPS = (1000, 750, 500, 250)
+LINGBOT_STEPS = tuple(1000 - i for i in (0, 179, 358, 679))
+
 WORKLOADS = {
     # the small fp32 case: 2 heads x 64, 4x4 tokens, chunk 2, sink 1, window 4, absolute RoPE, 8 chunks
     "tiny": Workload("tiny", Config(2, 64, 4, 4, 2, 1, 4, ROPE_ABS, F32), n_chunks=8, steady_chunk=1),
     # ABot-like 720P: 24 heads x 128, 22x40 tokens, chunk 3, window 21 incl. 5 reference sinks, relative RoPE
     "abot720": Workload("abot720", Config(24, 128, 22, 40, 3, 5, 21, ROPE_REL, BF16), n_chunks=40,
-                        prefill=5, steady_chunk=5),
+                        prefill=5, steady_chunk=5, timesteps=ABOT_STEPS),
     # LingBot-like 480P: 40 heads x 128, 30x52 tokens, chunk 4, window 18 incl. sink 6, absolute RoPE
-    "lb480": Workload("lb480", Config(40, 128, 30, 52, 4, 6, 18, ROPE_ABS, BF16), n_chunks=22, steady_chunk=4),
+    "lb480": Workload("lb480", Config(40, 128, 30, 52, 4, 6, 18, ROPE_ABS, BF16), n_chunks=22, steady_chunk=4,
+                      timesteps=LINGBOT_STEPS),
     # LingBot-like 720P: 40 heads x 128, 45x80 tokens
-    "lb720": Workload("lb720", Config(40, 128, 45, 80, 4, 6, 18, ROPE_ABS, BF16), n_chunks=8, steady_chunk=4),
+    "lb720": Workload("lb720", Config(40, 128, 45, 80, 4, 6, 18, ROPE_ABS, BF16), n_chunks=8, steady_chunk=4,
+                      timesteps=LINGBOT_STEPS),
     # 40 layers of the 480P layer, cross attention to 512 cached text tokens, 300 chunks
     "fulldepth480": Workload("fulldepth480", Config(40, 128, 30, 52, 4, 6, 18, ROPE_ABS, BF16), n_chunks=300,
-                             text_tokens=512, layers=40, steady_chunk=4),
+                             text_tokens=512, layers=40, steady_chunk=4, timesteps=LINGBOT_STEPS),
     # small shapes: several 64-key tiles, ragged frame sizes, ring wrap-around
     "small_abs": Workload("small_abs", Config(3, 128, 7, 9, 2, 2, 7, ROPE_ABS, BF16), n_chunks=12, steady_chunk=3),
     "small_rel": Workload("small_rel", Config(3, 128, 5, 13, 3, 2, 9, ROPE_REL, BF16), n_chunks=10, prefill=2,

@@ -116,3 +116,30 @@ def test_cross_attention_validation():
     assert f(p, 8, p, p, 0, 40, 128, skv.BF16, p, nul) == skv.ERR_SHAPE
     assert f(p, 0, p, p, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_SHAPE
     assert f(p, 8, p, p, 512, 0, 128, skv.BF16, p, nul) == skv.ERR_CONFIG
+
+
+def test_sampler_step_validation():
+    """Every error path of sampler_step returns before anything is enqueued (no GPU needed)."""
+    p, q, nul = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000), ctypes.c_void_p(0)
+    f = skv.lib.sampler_step
+    ok = (p, p, nul, 1.0, p, 1024, 0.75, 0.5, skv.BF16, q, q, nul)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["x_t", "v_cond", "v_uncond", "cfg", "noise", "n", "sigma", "sigma_next", "dtype", "x0", "xn", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(x_t=nul) == skv.ERR_NULL
+    assert call(v_cond=nul) == skv.ERR_NULL
+    assert call(x0=nul, xn=nul) == skv.ERR_NULL
+    assert call(noise=nul) == skv.ERR_NULL                      # re-noised output without noise
+    assert call(x_t=ctypes.c_void_p(0x40008)) == skv.ERR_ALIGN
+    assert call(v_uncond=ctypes.c_void_p(0x40004)) == skv.ERR_ALIGN
+    assert call(xn=ctypes.c_void_p(0x50002)) == skv.ERR_ALIGN
+    assert call(dtype=7) == skv.ERR_CONFIG
+    assert call(sigma=float("nan")) == skv.ERR_CONFIG
+    assert call(cfg=float("inf")) == skv.ERR_CONFIG
+    assert call(n=-1) == skv.ERR_SHAPE
+    assert call(n=0) == skv.OK                                   # nothing to do, nothing enqueued
