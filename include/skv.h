@@ -155,6 +155,21 @@ skv_status kv_cache_stage_v(skv_cache* cache, const void* v_cur, int32_t n_frame
 skv_status chunk_attention(const skv_cache* cache, const void* q, const void* k_cur, const void* v_cur,
                            int32_t n_frames, void* out, void* stream);
 
+/* Several chunk_attention calls of one shape in one launch ([LB-fast] table of
+ * inference modes: causal_pretrain runs every step twice, with and without the
+ * prompt, for classifier-free guidance; each of the two keeps its own cache).
+ * caches[i], q[i], k_cur[i], v_cur[i], out[i] (host arrays of n_caches device
+ * pointers, 1 <= n_caches <= 4) mean what they mean for chunk_attention; v_cur
+ * may be NULL (every element uses its staged values) and so may any v_cur[i].
+ * Every handle must have the same configuration (SKV_ERR_CONFIG otherwise) and
+ * appear once (SKV_ERR_STATE).  All elements are checked before anything is
+ * enqueued; then given values are staged and one kernel covers all elements
+ * (bf16; fp32 launches once per element).  A failed launch poisons every
+ * handle of the batch. */
+skv_status chunk_attention_batch(const skv_cache* const* caches, int32_t n_caches, const void* const* q,
+                                 const void* const* k_cur, const void* const* v_cur, int32_t n_frames,
+                                 void* const* out, void* stream);
+
 /* Cross attention over cached text K/V ([LB-causal] CrossAttention_KVCache;
  * [ABot-stream] 512 text tokens computed once): out = softmax(q K_text^T / sqrt(D)) V_text,
  * no rotary embedding, no mask.  q/out [n_q, H, D]; k_text/v_text [n_text, H, D].

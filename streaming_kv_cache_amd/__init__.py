@@ -25,6 +25,7 @@ EXPORTED = (
     "skv_abi_version", "skv_status_string", "kv_cache_bytes", "kv_cache_init", "kv_cache_reset",
     "kv_cache_destroy", "kv_cache_append_evict", "rope_apply", "rope_apply_window", "chunk_attention",
     "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v", "sampler_step",
+    "chunk_attention_batch",
 )
 
 
@@ -74,6 +75,8 @@ def _load() -> ctypes.CDLL:
         "kv_cache_info": ([vp, ctypes.POINTER(KvCacheInfo)], st),
         "kv_cache_gather": ([vp, vp, vp, ctypes.POINTER(ctypes.c_int64), vp], st),
         "kv_cache_stage_v": ([vp, vp, i32, vp], st),
+        "chunk_attention_batch": ([ctypes.POINTER(vp), i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                   i32, ctypes.POINTER(vp), vp], st),
         "sampler_step": ([vp, vp, vp, ctypes.c_double, vp, i64, ctypes.c_double, ctypes.c_double, i32, vp, vp, vp],
                          st),
     }
@@ -239,6 +242,27 @@ class KVCache:
         if n:
             _check(lib.kv_cache_gather(self._h, _ptr(k), _ptr(v), ids, _stream(stream)), "kv_cache_gather")
         return k, v, [int(ids[i]) for i in range(n)]
+
+
+def chunk_attention_batch(caches, qs, ks, vs, outs=None, stream=None):
+    """chunk_attention for several caches of one configuration in one launch (e.g. the two caches of
+    classifier-free guidance).  ``vs`` may be None or hold None entries (use the staged values)."""
+    n = len(caches)
+    if not (len(qs) == len(ks) == n and (vs is None or len(vs) == n)):
+        raise ValueError("one q, k_cur (and v_cur) per cache")
+    c = caches[0].cfg.chunk_frames
+    for i, cache in enumerate(caches):
+        cache._tensor(qs[i], c, "q")
+        cache._tensor(ks[i], c, "k_cur")
+        if vs is not None and vs[i] is not None:
+            cache._tensor(vs[i], c, "v_cur")
+    outs = [torch.empty_like(q) for q in qs] if outs is None else list(outs)
+    arr = lambda ptrs: (ctypes.c_void_p * n)(*[p.value for p in ptrs])  # noqa: E731
+    vp = None if vs is None else arr([_ptr(v) for v in vs])
+    _check(lib.chunk_attention_batch(arr([cache._h for cache in caches]), n, arr([_ptr(q) for q in qs]),
+                                     arr([_ptr(k) for k in ks]), vp, c, arr([_ptr(o) for o in outs]),
+                                     _stream(stream)), "chunk_attention_batch")
+    return outs
 
 
 def cross_attention(q: torch.Tensor, k_text: torch.Tensor, v_text: torch.Tensor,

@@ -371,7 +371,7 @@ __device__ __forceinline__ float half_swap_max(float x) { return fmaxf(x, xor32(
 __device__ __forceinline__ float half_swap_sum(float x) { return x + xor32(x); }
 
 template <int D, int NW, int NSTAGE>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(AttnBatch ab) {
   static_assert(NSTAGE == 2 || NSTAGE == 4, "two or four stages");
   constexpr int BM = NW * 32;
   constexpr int KP = 2 * D + 16;          // LDS pitch of a K row (bytes): data + one 16-byte pad
@@ -392,9 +392,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
   const int l32 = lane & 31, hf = lane >> 5;
-  const int n_qt = (a.Lq + BM - 1) / BM;
-  const int tile = xcd_remap(blockIdx.x, n_qt * a.H);
-  const int h = tile / n_qt, qt = tile - h * n_qt;
+  // every batch element has the same Lq and H
+  const int n_qt = (ab.b[0].Lq + BM - 1) / BM;
+  const int per = n_qt * ab.b[0].H;
+  const int tile = xcd_remap(blockIdx.x, per * ab.nb);
+  const int bi = tile / per, rest = tile - bi * per;
+  const AttnArgs& a = ab.b[bi];
+  const int h = rest / n_qt, qt = rest - h * n_qt;
   const int q_base = qt * BM + wave * 32;
   const float sl2 = a.sl2;
 
@@ -756,8 +760,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 // queries and loads run two tiles ahead).  The larger one runs about 10% faster per query once
 // the grid fills the chip; with few query tiles its coarser grid leaves CUs idle, so pick by
 // the number of dispatch rounds each needs on 256 CUs.
-hipError_t launch_attention_bf16_vt(const AttnArgs& a, int D, hipStream_t stream) {
-  const int64_t wg4 = (int64_t)((a.Lq + 127) / 128) * a.H, wg8 = (int64_t)((a.Lq + 255) / 256) * a.H;
+hipError_t launch_attention_bf16_vt(const AttnBatch& a, int D, hipStream_t stream) {
+  const AttnArgs& a0 = a.b[0];
+  const int64_t wg4 = (int64_t)((a0.Lq + 127) / 128) * a0.H * a.nb, wg8 = (int64_t)((a0.Lq + 255) / 256) * a0.H * a.nb;
   const double rounds4 = (double)((wg4 + 511) / 512), rounds8 = 0.9 * (double)((wg8 + 255) / 256);
   // SKV_ATTN_WAVES=4 or 8 forces one shape (tests cover both on small inputs)
   const char* env = std::getenv("SKV_ATTN_WAVES");

@@ -60,6 +60,15 @@ struct AttnArgs {
   float sl2;       // softmax scale * log2(e)
 };
 
+// Up to kMaxAttnBatch independent attention problems of one shape (same Lq, H, D) in one
+// launch, e.g. the conditional and unconditional caches of guidance: workgroup ids cover the
+// query tiles of element 0, then of element 1, ...
+constexpr int kMaxAttnBatch = 4;
+struct AttnBatch {
+  AttnArgs b[kMaxAttnBatch];
+  int32_t nb;
+};
+
 // Bijective remap of a workgroup id so that workgroups the dispatcher sends to
 // the same XCD (ids congruent mod 8) work on consecutive tiles.
 __device__ __forceinline__ int xcd_remap(int pid, int total) {

@@ -284,9 +284,9 @@ skv_status rope_apply_window(skv_cache* c, void* stream) {
   return SKV_OK;
 }
 
-skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur, const void* v_cur,
-                           int32_t n_frames, void* out, void* stream) {
-  skv_cache* c = const_cast<skv_cache*>(cc);
+// Checks one chunk_attention call and describes its key ranges; enqueues nothing.
+static skv_status attention_args(skv_cache* c, const void* q, const void* k_cur, const void* v_cur, int32_t n_frames,
+                                 void* out, skv::AttnArgs* a) {
   skv_status st = check_handle(c);
   if (st != SKV_OK) return st;
   if ((st = check_ptr(q)) != SKV_OK) return st;
@@ -300,19 +300,12 @@ skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur
   if (rel && p.n_hist > 0 && !c->window_ready) return SKV_ERR_STATE;
   if (!v_cur && !c->v_staged) return SKV_ERR_STATE;
 
-  if (v_cur) {
-    st = stage_v(c, v_cur, stream);
-    if (st != SKV_OK) return st;
-    c->v_staged = true;
-  }
-
-  skv::AttnArgs a;
-  a.q = q;
-  a.out = out;
-  a.Lq = g.c * g.F;
-  a.H = g.H;
-  a.sl2 = softmax_scale_log2(g.D);
-  a.nseg = 0;
+  a->q = q;
+  a->out = out;
+  a->Lq = g.c * g.F;
+  a->H = g.H;
+  a->sl2 = softmax_scale_log2(g.D);
+  a->nseg = 0;
   const int64_t store_hs = (int64_t)g.W * g.F * g.D;
   const int64_t ws_hs = (int64_t)(g.W - g.c) * g.F * g.D;
   const int per16 = 16 / g.elt;
@@ -334,7 +327,7 @@ skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur
     sg.v_ds = vt_row(g);
     sg.n = r.frames * g.F;
     sg.v_al16 = (key0 % per16 == 0 && vt_row(g) % per16 == 0) ? 1 : 0;
-    a.seg[a.nseg++] = sg;
+    a->seg[a->nseg++] = sg;
   }
   skv::KvSeg cur;
   cur.k = k_cur;
@@ -346,11 +339,59 @@ skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur
   cur.v_ds = cur_row(g);
   cur.n = g.c * g.F;
   cur.v_al16 = 1;
-  a.seg[a.nseg++] = cur;
-  for (int i = a.nseg; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
-  const hipError_t e = g.dtype == SKV_BF16 ? skv::launch_attention_bf16_vt(a, g.D, (hipStream_t)stream)
-                                            : skv::launch_attention_f32(a, g.D, (hipStream_t)stream);
-  return launched(c, e);
+  a->seg[a->nseg++] = cur;
+  for (int i = a->nseg; i < 4; ++i) a->seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  return SKV_OK;
+}
+
+static bool same_geometry(const skv::Geometry& x, const skv::Geometry& y) {
+  return x.H == y.H && x.D == y.D && x.gh == y.gh && x.gw == y.gw && x.c == y.c && x.S == y.S && x.W == y.W &&
+         x.dtype == y.dtype && x.mode == y.mode;
+}
+
+skv_status chunk_attention_batch(const skv_cache* const* caches, int32_t n_caches, const void* const* q,
+                                 const void* const* k_cur, const void* const* v_cur, int32_t n_frames,
+                                 void* const* out, void* stream) {
+  if (!caches || !q || !k_cur || !out) return SKV_ERR_NULL;
+  if (n_caches < 1 || n_caches > skv::kMaxAttnBatch) return SKV_ERR_SHAPE;
+  skv::AttnBatch ab{};
+  ab.nb = n_caches;
+  skv_cache* cs[skv::kMaxAttnBatch];
+  for (int i = 0; i < n_caches; ++i) {
+    cs[i] = const_cast<skv_cache*>(caches[i]);
+    if (!cs[i]) return SKV_ERR_NULL;
+    for (int j = 0; j < i; ++j)
+      if (cs[j] == cs[i]) return SKV_ERR_STATE;  // one handle twice: its staged values would clash
+    const skv_status st = attention_args(cs[i], q[i], k_cur[i], v_cur ? v_cur[i] : nullptr, n_frames, out[i],
+                                         &ab.b[i]);
+    if (st != SKV_OK) return st;
+    if (!same_geometry(cs[i]->g, cs[0]->g)) return SKV_ERR_CONFIG;
+  }
+  // everything checked: stage the values given, then one launch for all elements
+  for (int i = 0; i < n_caches; ++i)
+    if (v_cur && v_cur[i]) {
+      const skv_status st = stage_v(cs[i], v_cur[i], stream);
+      if (st != SKV_OK) return st;
+      cs[i]->v_staged = true;
+    }
+  const skv::Geometry& g = cs[0]->g;
+  hipError_t e = hipSuccess;
+  if (g.dtype == SKV_BF16) {
+    e = skv::launch_attention_bf16_vt(ab, g.D, (hipStream_t)stream);
+  } else {
+    for (int i = 0; i < n_caches && e == hipSuccess; ++i) e = skv::launch_attention_f32(ab.b[i], g.D, (hipStream_t)stream);
+  }
+  skv_status st = SKV_OK;
+  for (int i = 0; i < n_caches; ++i) {
+    const skv_status si = launched(cs[i], e);
+    if (si != SKV_OK) st = si;
+  }
+  return st;
+}
+
+skv_status chunk_attention(const skv_cache* cc, const void* q, const void* k_cur, const void* v_cur,
+                           int32_t n_frames, void* out, void* stream) {
+  return chunk_attention_batch(&cc, 1, &q, &k_cur, &v_cur, n_frames, &out, stream);
 }
 
 skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const void* v_text, int32_t n_text,

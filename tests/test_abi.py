@@ -143,3 +143,31 @@ def test_sampler_step_validation():
     assert call(cfg=float("inf")) == skv.ERR_CONFIG
     assert call(n=-1) == skv.ERR_SHAPE
     assert call(n=0) == skv.OK                                   # nothing to do, nothing enqueued
+
+
+def test_chunk_attention_batch_validation():
+    """Batch checks return before anything is enqueued (fake aligned device addresses, no GPU)."""
+    V = ctypes.c_void_p
+    p, nul = V(0x40000), V(0)
+    st, h1 = _init(LB480)
+    st2, h2 = _init(LB480, k=0x50000, v=0x60000, ws=0x70000)
+    st3, h3 = _init(skv.Config(40, 128, 30, 52, 4, 6, 20), k=0x80000, v=0x90000, ws=0xA0000)
+    assert st == st2 == st3 == skv.OK
+    f = skv.lib.chunk_attention_batch
+
+    def arr(*xs):
+        return (V * len(xs))(*[x.value for x in xs])
+
+    two = arr(p, p)
+    assert f(None, 2, two, two, two, 4, two, nul) == skv.ERR_NULL
+    assert f(arr(h1, h2), 0, two, two, two, 4, two, nul) == skv.ERR_SHAPE
+    five = arr(h1, h2, h1, h2, h1)
+    assert f(five, 5, five, five, five, 4, five, nul) == skv.ERR_SHAPE
+    assert f(arr(h1, nul), 2, two, two, two, 4, two, nul) == skv.ERR_NULL
+    assert f(arr(h1, h1), 2, two, two, two, 4, two, nul) == skv.ERR_STATE       # one handle twice
+    assert f(arr(h1, h3), 2, two, two, two, 4, two, nul) == skv.ERR_CONFIG      # different windows
+    assert f(arr(h1, h2), 2, two, two, None, 4, two, nul) == skv.ERR_STATE      # nothing staged
+    assert f(arr(h1, h2), 2, two, arr(p, nul), two, 4, two, nul) == skv.ERR_NULL
+    assert f(arr(h1, h2), 2, two, two, two, 3, two, nul) == skv.ERR_SHAPE
+    for h in (h1, h2, h3):
+        skv.lib.kv_cache_destroy(h)
