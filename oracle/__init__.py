@@ -22,5 +22,7 @@ from .skv_oracle import (  # noqa: F401
     visible_history,
     attention,
     cross_attention,
+    block_causal_visible,
+    block_causal_attention,
     StreamingOracle,
 )

@@ -193,6 +193,62 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return out
 
 
+def block_causal_visible(n_frames: int, q_frame0: int, chunk_frames: int, sink_frames: int,
+                         window_frames: int) -> np.ndarray:
+    """[n_frames - q_frame0, n_frames] boolean: may query frame i (row i - q_frame0) see key frame j?
+
+    [ABot-stream] 机制二 (block-causal mask: a chunk's queries see their own chunk and
+    the window of earlier chunks, frames of a chunk see each other; the same structure
+    in training, with FlexAttention's block_mask) and [LB-fast] "3. KV 缓存 滚动窗口"
+    (the window keeps the sink frames and the most recent frames).  Query frame i lies
+    in the chunk ending (exclusive) at e = q_frame0 + c * ((i - q_frame0) // c + 1);
+    it sees key frame j iff j < e and (j < S or j >= e - (W - S)): the sinks plus the
+    last W - S frames up to its chunk's end, i.e. exactly what streaming chunk by chunk
+    shows that chunk.
+    """
+    if (n_frames - q_frame0) % chunk_frames or not 0 <= q_frame0 < n_frames:
+        raise ValueError("query frames must be whole chunks")
+    i = np.arange(q_frame0, n_frames)[:, None]
+    j = np.arange(n_frames)[None, :]
+    e = q_frame0 + chunk_frames * ((i - q_frame0) // chunk_frames + 1)
+    return (j < e) & ((j < sink_frames) | (j >= e - (window_frames - sink_frames)))
+
+
+def block_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, frame_tokens: int, chunk_frames: int,
+                           sink_frames: int, window_frames: int, q_frame0: int = 0,
+                           rows: Optional[np.ndarray] = None, block_rows: int = 1024) -> np.ndarray:
+    """Many chunks at once under the sink + window block-causal mask (plain definition).
+
+    q: the already-rotated queries of frames q_frame0 .. n_frames-1 ([(n - q0) F, H, D]);
+    k, v: the already-rotated keys and the values of all n frames ([n F, H, D]).  Each
+    query row is a softmax over the keys its frame may see (``block_causal_visible``),
+    scaled by 1/sqrt(D).  ``rows`` selects query rows.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    f = int(frame_tokens)
+    n = k.shape[0] // f
+    vis = block_causal_visible(n, q_frame0, chunk_frames, sink_frames, window_frames)
+    row_ids = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    q = q[row_ids]
+    lq, h, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    key_frame = np.arange(n * f) // f
+    out = np.empty((lq, h, v.shape[2]), dtype=np.float64)
+    for r0 in range(0, lq, block_rows):
+        rr = row_ids[r0:r0 + block_rows]
+        allowed = vis[rr // f][:, key_frame]          # [rows, keys]
+        for hh in range(h):
+            s = (q[r0:r0 + block_rows, hh, :] @ k[:, hh, :].T) * scale
+            s = np.where(allowed, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[r0:r0 + block_rows, hh, :] = p @ v[:, hh, :]
+    return out
+
+
 def cross_attention(q: np.ndarray, k_text: np.ndarray, v_text: np.ndarray,
                     rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Attention of video queries over cached text keys/values: no RoPE, no mask.

@@ -256,6 +256,51 @@ def check_sink_window_mask():
         assert np.allclose(got, ref, atol=1e-11), (cfg, np.abs(got - ref).max())
 
 
+def check_block_causal_matches_streaming():
+    """The many-chunk masked attention equals streaming the same sequence chunk by chunk (abs)."""
+    for cfg, n_chunks, prefill in (((2, 64, 2, 2, 2, 1, 4, "abs"), 8, 0),
+                                   ((2, 32, 2, 3, 3, 5, 11, "abs"), 7, 5),
+                                   ((1, 64, 1, 3, 4, 6, 18, "abs"), 9, 0),
+                                   ((1, 32, 2, 2, 2, 0, 3, "abs"), 6, 0)):
+        h, d, gh, gw, c, s, w, _ = cfg
+        f = gh * gw
+        outs, raws, _ = _stream(cfg, n_chunks, seed=10, prefill=prefill)
+        k_all = np.concatenate([r[1] for r in raws])
+        v_all = np.concatenate([r[2] for r in raws])
+        n = k_all.shape[0] // f
+        k_rot = so.rope_3d(k_all, range(n), gh, gw)
+        q_rot = np.concatenate([so.rope_3d(r[0], range(prefill + i * c, prefill + (i + 1) * c), gh, gw)
+                                for i, r in enumerate(raws[1:] if prefill else raws)])
+        got = so.block_causal_attention(q_rot, k_rot, v_all, f, c, s, w, q_frame0=prefill)
+        assert np.allclose(got, np.concatenate(outs), atol=1e-11), (cfg, np.abs(got - np.concatenate(outs)).max())
+        # a row subset gives the same rows
+        rows = np.array([0, 5, got.shape[0] - 1])
+        sub = so.block_causal_attention(q_rot, k_rot, v_all, f, c, s, w, q_frame0=prefill, rows=rows)
+        assert np.allclose(sub, got[rows], atol=1e-13)
+
+
+def check_block_causal_counts_and_full():
+    """Each query frame sees min(e, W) frames (e = its chunk's end); one chunk with a large window is
+    plain full attention (torch scaled_dot_product_attention, fp64, no mask)."""
+    import torch
+    for n, q0, c, s, w in ((20, 0, 4, 6, 18), (23, 5, 3, 5, 21), (9, 1, 2, 0, 5), (12, 0, 2, 3, 5)):
+        vis = so.block_causal_visible(n, q0, c, s, w)
+        for row, i in enumerate(range(q0, n)):
+            e = q0 + c * ((i - q0) // c + 1)
+            assert vis[row].sum() == min(e, w), (n, q0, c, s, w, i)
+            assert vis[row, :s].all() or e < s        # sinks stay visible
+            assert not vis[row, e:].any()             # nothing after the chunk's end
+    r = _rng(11)
+    f, h, d = 6, 2, 32
+    q = r.standard_normal((3 * f, h, d))
+    k = r.standard_normal((3 * f, h, d))
+    v = r.standard_normal((3 * f, h, d))
+    got = so.block_causal_attention(q, k, v, f, 3, 1, 8, q_frame0=0)
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).permute(1, 0, 2).numpy()
+    assert np.allclose(got, ref, atol=1e-12)
+
+
 def check_rel_equals_abs_cases():
     """rel == abs when nothing was evicted yet, and when there are no sinks (shift invariance)."""
     for s, w, n_chunks in ((1, 64, 5), (0, 5, 9), (0, 7, 8)):
@@ -386,5 +431,6 @@ ALL_CHECKS = [
     check_rope_relative_shift, check_rope_split_figures, check_cache_closed_form, check_cache_rejects_oversize,
     check_sink_identity, check_visible_matches_append_then_slice, check_full_window_block_causal,
     check_sink_window_mask, check_rel_equals_abs_cases, check_rel_ids_bounded, check_probe_zero_query,
-    check_probe_onehot, check_sdpa, check_page_figures,
+    check_probe_onehot, check_sdpa, check_page_figures, check_block_causal_matches_streaming,
+    check_block_causal_counts_and_full,
 ]

@@ -34,6 +34,11 @@ MUTATIONS = {
     "rel_ids_frame_based": ("k_hist = [self._rope(e[1], self._clamp([j])) for j, e in enumerate(hist)]",
                             "k_hist = [self._rope(e[1], self._clamp([e[0]])) for j, e in enumerate(hist)]"),
     "rel_query_ids_off": ("return self._clamp(range(nv - self.c, nv))", "return self._clamp(range(nv - self.c - 1, nv - 1))"),
+    "bc_chunk_end_early": ("e = q_frame0 + chunk_frames * ((i - q_frame0) // chunk_frames + 1)",
+                           "e = q_frame0 + chunk_frames * ((i - q_frame0) // chunk_frames)"),
+    "bc_window_short": ("(j >= e - (window_frames - sink_frames))", "(j >= e - (window_frames - sink_frames) + 1)"),
+    "bc_no_sinks": ("(j < sink_frames) | (j >= e", "(j < 0) | (j >= e"),
+    "bc_frame_causal": ("return (j < e) &", "return (j <= i) &"),
     "abs_stores_raw": ("if self.mode == \"abs\":\n            f0 = self.n_appended", "if False:\n            f0 = self.n_appended"),
 }
 
