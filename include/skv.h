@@ -187,6 +187,27 @@ skv_status kv_cache_info(const skv_cache* cache, kv_cache_info_t* info);
 skv_status kv_cache_gather(const skv_cache* cache, void* k_out, void* v_out, int64_t* frame_ids_host,
                            void* stream);
 
+/* Many chunks at once under the sink + window block-causal mask ([ABot-stream]
+ * 机制二: a chunk's queries see their own chunk and the window of earlier chunks,
+ * frames inside a chunk see each other; the same mask serves training, where it is
+ * FlexAttention's block_mask.  [LB-fast] "3. KV 缓存 滚动窗口": the window keeps the
+ * first S frames and the most recent frames).  No cache handle: cfg gives H, D,
+ * F = grid_h * grid_w, c, S, W and dtype (bf16 only).
+ * k, v: [n_frames*F, H, D], the keys already rotated (e.g. rope_apply at absolute
+ * frame ids); q, out: [(n_frames - q_frame0)*F, H, D], the rotated queries of frames
+ * q_frame0 .. n_frames-1 (frames before q_frame0 are context only, e.g. reference
+ * sinks).  Query frame i lies in the chunk ending at e = q_frame0 + c*((i-q_frame0)/c + 1)
+ * and sees key frame j iff j < e and (j < S or j >= e - (W - S)): exactly the keys a
+ * chunk sees when it is streamed through a cache with S sinks and window W.
+ * workspace: block_causal_workspace_bytes(cfg, n_frames) bytes of device memory
+ * (the values are transposed there first).  Requires (n_frames - q_frame0) % c == 0.
+ * Errors: SKV_ERR_NULL / SKV_ERR_ALIGN on pointers; SKV_ERR_CONFIG for an invalid or
+ * non-bf16 cfg; SKV_ERR_SHAPE for frame counts out of range or a sequence too long
+ * for 32-bit offsets within one head. */
+skv_status block_causal_workspace_bytes(const skv_config* cfg, int32_t n_frames, size_t* bytes);
+skv_status block_causal_attention(const skv_config* cfg, const void* q, const void* k, const void* v,
+                                  int32_t n_frames, int32_t q_frame0, void* workspace, void* out, void* stream);
+
 /* One step of the few-step sampler between attention passes ([LB-fast]
  * "2. 4 步采样": the forward gives a flow-matching velocity, x0 is recovered in
  * one step and re-noised to the next, smaller timestep unless it was the last;

@@ -25,7 +25,7 @@ EXPORTED = (
     "skv_abi_version", "skv_status_string", "kv_cache_bytes", "kv_cache_init", "kv_cache_reset",
     "kv_cache_destroy", "kv_cache_append_evict", "rope_apply", "rope_apply_window", "chunk_attention",
     "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v", "sampler_step",
-    "chunk_attention_batch",
+    "chunk_attention_batch", "block_causal_workspace_bytes", "block_causal_attention",
 )
 
 
@@ -77,6 +77,8 @@ def _load() -> ctypes.CDLL:
         "kv_cache_stage_v": ([vp, vp, i32, vp], st),
         "chunk_attention_batch": ([ctypes.POINTER(vp), i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                    i32, ctypes.POINTER(vp), vp], st),
+        "block_causal_workspace_bytes": ([ctypes.POINTER(SkvConfig), i32, ctypes.POINTER(ctypes.c_size_t)], st),
+        "block_causal_attention": ([ctypes.POINTER(SkvConfig), vp, vp, vp, i32, i32, vp, vp, vp], st),
         "sampler_step": ([vp, vp, vp, ctypes.c_double, vp, i64, ctypes.c_double, ctypes.c_double, i32, vp, vp, vp],
                          st),
     }
@@ -263,6 +265,35 @@ def chunk_attention_batch(caches, qs, ks, vs, outs=None, stream=None):
                                      arr([_ptr(k) for k in ks]), vp, c, arr([_ptr(o) for o in outs]),
                                      _stream(stream)), "chunk_attention_batch")
     return outs
+
+
+def block_causal_workspace_bytes(cfg: Config, n_frames: int) -> int:
+    c = cfg.c_struct()
+    b = ctypes.c_size_t()
+    _check(lib.block_causal_workspace_bytes(ctypes.byref(c), int(n_frames), ctypes.byref(b)),
+           "block_causal_workspace_bytes")
+    return b.value
+
+
+def block_causal_attention(cfg: Config, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_frame0: int = 0,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Many chunks at once under the sink + window block-causal mask (see skv.h).  k, v: all frames;
+    q: frames q_frame0.. ; everything already rotated."""
+    f = cfg.tokens_per_frame
+    n = k.shape[0] // f
+    for name, t, rows in (("k", k, n * f), ("v", v, n * f), ("q", q, (n - q_frame0) * f)):
+        if tuple(t.shape) != (rows, cfg.heads, cfg.head_dim) or t.dtype != cfg.torch_dtype or not t.is_cuda \
+                or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous {cfg.torch_dtype} CUDA tensor of shape "
+                             f"{(rows, cfg.heads, cfg.head_dim)}")
+    if workspace is None:
+        workspace = torch.empty(block_causal_workspace_bytes(cfg, n), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q) if out is None else out
+    c = cfg.c_struct()
+    _check(lib.block_causal_attention(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), n, int(q_frame0), _ptr(workspace),
+                                      _ptr(out), _stream(stream)), "block_causal_attention")
+    return out
 
 
 def cross_attention(q: torch.Tensor, k_text: torch.Tensor, v_text: torch.Tensor,

@@ -370,7 +370,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 __device__ __forceinline__ float half_swap_max(float x) { return fmaxf(x, xor32(x)); }
 __device__ __forceinline__ float half_swap_sum(float x) { return x + xor32(x); }
 
-template <int D, int NW, int NSTAGE>
+template <int D, int NW, int NSTAGE, bool MASKED>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(AttnBatch ab) {
   static_assert(NSTAGE == 2 || NSTAGE == 4, "two or four stages");
   constexpr int BM = NW * 32;
@@ -421,7 +421,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
-  float m_run = 0.f, l_run = 0.f;
+  // unmasked: the running max starts at the first half tile's max; masked: at -inf (a row may
+  // see no key of the first tiles) and follows every half tile's max
+  float m_run = MASKED ? -INFINITY : 0.f, l_run = 0.f;
+
+  // Masked (many chunks at once): query row r lies in frame q0 + r / F of the chunk ending at
+  // frame e(r); it sees keys of frames j < e with j < S or j >= e - (W - S).  This workgroup's
+  // keys are the visible sinks [0, min(S, e_b) F) and the window [max(S, e_a - (W - S)) F, e_b F),
+  // e_a / e_b the chunk ends of its first / last rows; lanes mask what their own row may not see.
+  int e_a = 0, e_b = 0, sink_keys = 0, ring0 = 0, ring_keys = 0, vis_hi = 0, ring_lo = 0;
+  if constexpr (MASKED) {
+    const int r_last = (qt * BM + BM < a.Lq ? qt * BM + BM : a.Lq) - 1;
+    auto chunk_end = [&](int row) { return a.mq0 + a.mc * ((row / a.mF) / a.mc + 1); };
+    e_a = chunk_end(qt * BM);
+    e_b = chunk_end(r_last);
+    sink_keys = (a.mS < e_b ? a.mS : e_b) * a.mF;
+    const int r0f = a.mS > e_a - (a.mW - a.mS) ? a.mS : e_a - (a.mW - a.mS);
+    ring0 = r0f * a.mF;
+    ring_keys = e_b * a.mF - ring0 > 0 ? e_b * a.mF - ring0 : 0;
+    const int qr = q_base + l32 < a.Lq ? q_base + l32 : r_last;
+    const int er = chunk_end(qr);
+    vis_hi = er * a.mF;
+    ring_lo = (a.mS > er - (a.mW - a.mS) ? a.mS : er - (a.mW - a.mS)) * a.mF;
+  }
+  const int nseg = MASKED ? 2 : a.nseg;
 
   // Lane part of the direct loads.  Lane l of block blk fills LDS bytes [blk*1024 + 16 l, +16);
   // lanes that land on a pad chunk fetch a harmless valid chunk (row 0, chunk 0).
@@ -442,19 +465,23 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   int kq_off[KI], vq_off[VI];  // byte offsets for whole tiles of the current range
 
   // Two uniform tile iterators over the key ranges: K runs ahead of V.
+  auto seg_n = [&](int s_) -> int { return MASKED ? (s_ == 0 ? sink_keys : ring_keys) : a.seg[s_].n; };
+  auto seg_start = [&](int s_) -> int { return MASKED ? (s_ == 0 ? 0 : ring0) : 0; };
   int n_tiles = 0;
-  for (int s_ = 0; s_ < a.nseg; ++s_) n_tiles += (a.seg[s_].n + kBN - 1) / kBN;
+  for (int s_ = 0; s_ < nseg; ++s_) n_tiles += (seg_n(s_) + kBN - 1) / kBN;
   if (n_tiles == 0) return;  // no keys: the host never launches this
   int ksi = 0, krem = 0, k_rs_b = 0;
   const uint8_t* kp = nullptr;
   
-  int k_so = 0;
+  int k_so = 0, kkey = 0;  // kkey: sequence index of the next K tile's first key (masked)
   auto k_seg = [&](int s_) {
-    const KvSeg sg = a.seg[s_];
-    kp = (const uint8_t*)sg.k + 2 * (int64_t)h * sg.k_hs;
+    const KvSeg sg = a.seg[MASKED ? 0 : s_];
+    const int start = seg_start(s_);
+    kp = (const uint8_t*)sg.k + 2 * ((int64_t)h * sg.k_hs + (int64_t)start * sg.k_rs);
     k_so = 0;
+    kkey = start;
     k_rs_b = (int)(2 * sg.k_rs);
-    krem = sg.n;
+    krem = seg_n(s_);
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       int row, c16;
@@ -467,12 +494,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   
   int v_so = 0;
   auto v_seg = [&](int s_) {
-    const KvSeg sg = a.seg[s_];
-    vp = (const uint8_t*)sg.v + 2 * (int64_t)h * sg.v_hs;
+    const KvSeg sg = a.seg[MASKED ? 0 : s_];
+    const int start = seg_start(s_);
+    vp = (const uint8_t*)sg.v + 2 * ((int64_t)h * sg.v_hs + (int64_t)start * sg.v_rs);
     v_so = 0;
     v_ds_b = (int)(2 * sg.v_ds);
-    vrem = sg.n;
-    v_al16 = sg.v_al16;
+    vrem = seg_n(s_);
+    v_al16 = sg.v_al16 && (start & 7) == 0;
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       int d, ch;
@@ -481,13 +509,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     }
   };
   k_seg(0);
-  while (krem <= 0 && ++ksi < a.nseg) k_seg(ksi);
+  while (krem <= 0 && ++ksi < nseg) k_seg(ksi);
   v_seg(0);
-  while (vrem <= 0 && ++vsi < a.nseg) v_seg(vsi);
+  while (vrem <= 0 && ++vsi < nseg) v_seg(vsi);
 
-  // Issue the next K tile into stage st; returns its valid key count.
+  // Issue the next K tile into stage st; returns its valid key count (and, masked, the
+  // sequence index of its first key in key0).
+  int key0 = 0;
   auto issue_k = [&](int st) -> int {
     const int nk = krem < kBN ? krem : kBN;
+    key0 = kkey;
+    kkey += kBN;
     uint8_t* dst = smem + st * KT_B;
     if (nk == kBN) {
 #pragma unroll
@@ -512,7 +544,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     krem -= kBN;
     kp += kBN * k_rs_b;
     k_so += kBN * k_rs_b;
-    while (krem <= 0 && ++ksi < a.nseg) k_seg(ksi);
+    while (krem <= 0 && ++ksi < nseg) k_seg(ksi);
     return nk;
   };
   // Issue the next V^T tile into stage st.
@@ -549,7 +581,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     vrem -= kBN;
     vp += 2 * kBN;
     v_so += 2 * kBN;
-    while (vrem <= 0 && ++vsi < a.nseg) v_seg(vsi);
+    while (vrem <= 0 && ++vsi < nseg) v_seg(vsi);
   };
 
   // per-lane LDS byte offsets of the A operands (plus immediates per k-step)
@@ -561,24 +593,29 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 
   // Two stages: K runs one half-tile ahead of V (K0, V0, K1 in flight at the start), two
   // barriers per tile.  Four stages: whole tiles NSTAGE-2 ahead, one barrier per tile.
-  int nk_k[2] = {0, 0};      // two stages: valid keys of the K tile in each stage
-  int nkq[3] = {0, 0, 0};    // four stages: valid keys of the next tiles, oldest first
+  int nk_k[2] = {0, 0}, k0_k[2] = {0, 0};        // two stages: per stage
+  int nkq[3] = {0, 0, 0}, k0q[3] = {0, 0, 0};    // four stages: the next tiles, oldest first
   if constexpr (NSTAGE == 2) {
     nk_k[0] = issue_k(0);
+    k0_k[0] = key0;
     issue_v(0);
-    if (n_tiles > 1) nk_k[1] = issue_k(1);
+    if (n_tiles > 1) {
+      nk_k[1] = issue_k(1);
+      k0_k[1] = key0;
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < NSTAGE - 1; ++i)
       if (i < n_tiles) {
         nkq[i] = issue_k(i);
+        k0q[i] = key0;
         issue_v(i);
       }
   }
 
-  // P = exp2(S' - m_run) for one 32-key half, packed to bf16 in B-operand order; returns the
+  // P = exp2(S' - sub) for one 32-key half, packed to bf16 in B-operand order; returns the
   // row sum of the rounded values.
-  auto exp_half = [&](const f32x16_t& sv, bf16x8_t& p0, bf16x8_t& p1) -> float {
+  auto exp_half = [&](const f32x16_t& sv, float sub, bf16x8_t& p0, bf16x8_t& p1) -> float {
     float ls = 0.f;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -586,7 +623,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 8 * half + 2 * e;
-        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sv[r] - m_run), __builtin_amdgcn_exp2f(sv[r + 1] - m_run));
+        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sv[r] - sub), __builtin_amdgcn_exp2f(sv[r + 1] - sub));
         ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, one2), ls,
                                              false);
         pk[e] = w;
@@ -611,11 +648,43 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
     m_run += up;
   };
+  // Masked: the running max follows the max of every half tile (rows may have seen nothing
+  // yet: -inf until their first visible key); returns the offset the exponentials use.
+  auto follow_max = [&](const f32x16_t& sv) -> float {
+    const float mn = fmaxf(m_run, max_half(sv));
+    if (__any(mn > m_run)) {
+      const float alpha = mn > m_run ? __builtin_amdgcn_exp2f(m_run - mn) : 1.f;  // m_run = -inf: 0
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+      m_run = mn;
+    }
+    return m_run == -INFINITY ? 0.f : m_run;
+  };
+  // Masked: scores of keys this lane's row may not see (or past the range) -> -inf.  kbase is the
+  // sequence index of the half tile's first key, nvalid its valid key count.
+  auto mask_half = [&](f32x16_t& sv, int kbase, int nvalid) {
+    const int kend = kbase + (nvalid < 32 ? nvalid : 32);
+    const bool all_seen = kend <= e_a * a.mF &&
+                          (kend <= a.mS * a.mF || kbase >= (a.mS > e_b - (a.mW - a.mS) ? a.mS : e_b - (a.mW - a.mS)) * a.mF);
+    if (all_seen && nvalid >= 32) return;
+    // key score_key(r, hf) = kbase + score_key(r, 0) + 8 hf: compare score_key(r, 0) with shifted bounds
+    const int off = kbase + 8 * hf;
+    int t_hi = vis_hi - off, t_sink = a.mS * a.mF - off, t_ring = ring_lo - off, t_n = nvalid - 8 * hf;
+    asm volatile("" : "+v"(t_hi), "+v"(t_sink), "+v"(t_ring), "+v"(t_n));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = score_key(r, 0);
+      if (!(kk < t_hi && kk < t_n && (kk < t_sink || kk >= t_ring))) sv[r] = -INFINITY;
+    }
+  };
 
   for (int t = 0; t < n_tiles; ++t) {
     const int st = NSTAGE == 2 ? (t & 1) : (t & 3);
     const bool more = t + 1 < n_tiles;
-    int nk;
+    int nk, k0;
     if constexpr (NSTAGE == 2) {
       // K_t landed (V_t and K_{t+1} may still be in flight), then everyone's V_{t-1} reads are done.
       if (more)
@@ -624,6 +693,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
         wait_vm_barrier<VMIN>();
       if (more) issue_v(st ^ 1);
       nk = nk_k[st];
+      k0 = k0_k[st];
     } else {
       // tile t landed (up to two later tiles may still be in flight), then everyone is done
       // with tile t-1, whose stage takes tile t+3
@@ -634,11 +704,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       else
         wait_vm_barrier<0>();
       nk = nkq[0];
+      k0 = k0q[0];
       nkq[0] = nkq[1];
       nkq[1] = nkq[2];
+      k0q[0] = k0q[1];
+      k0q[1] = k0q[2];
       if (t + NSTAGE - 1 < n_tiles) {
         const int sn = (t + NSTAGE - 1) & 3;
         nkq[2] = issue_k(sn);
+        k0q[2] = key0;
         issue_v(sn);
       }
     }
@@ -653,16 +727,23 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     f32x16_t s0 = {};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s0, 0, 0, 0);
-    if (nk < 32) {
-      int nkh = nk - 8 * hf;  // key score_key(r, hf) >= nk  <=>  score_key(r, 0) >= nk - 8 hf
-      asm volatile("" : "+v"(nkh));
+    float sub0;
+    if constexpr (MASKED) {
+      mask_half(s0, k0, nk);
+      sub0 = follow_max(s0);
+    } else {
+      if (nk < 32) {
+        int nkh = nk - 8 * hf;  // key score_key(r, hf) >= nk  <=>  score_key(r, 0) >= nk - 8 hf
+        asm volatile("" : "+v"(nkh));
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (score_key(r, 0) >= nkh) s0[r] = -INFINITY;
-    }
-    if (t == 0) {
-      // first tile: the running max starts at the max of its first half (key 0 is always valid)
-      m_run = max_half(s0);
+        for (int r = 0; r < 16; ++r)
+          if (score_key(r, 0) >= nkh) s0[r] = -INFINITY;
+      }
+      if (t == 0) {
+        // first tile: the running max starts at the max of its first half (key 0 is always valid)
+        m_run = max_half(s0);
+      }
+      sub0 = m_run;
     }
 
     // ---- keys 32..63 on the matrix cores while P of keys 0..31 is formed
@@ -673,7 +754,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s1, 0, 0, 0);
-    float lsum = exp_half(s0, pb[0], pb[1]);
+    float lsum = exp_half(s0, sub0, pb[0], pb[1]);
 #pragma unroll
     for (int i = 0; i < KSTEPS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -681,12 +762,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     }
     // The running max is raised only when some score exceeds it by a lot (a row sum past
     // 2^60): the result is the same for any max, and P stays far below overflow.
-    if (__any(lsum > 0x1p60f)) {
+    if (!MASKED && __any(lsum > 0x1p60f)) {
       raise_by(fmaxf(max_half(s0) - m_run, 0.f));
-      lsum = exp_half(s0, pb[0], pb[1]);
+      lsum = exp_half(s0, m_run, pb[0], pb[1]);
     }
     l_run += lsum;
-    if (nk < kBN) {
+    if constexpr (MASKED) {
+      mask_half(s1, k0 + 32, nk - 32);
+    } else if (nk < kBN) {
       int nkh = nk - 32 - 8 * hf;
       asm volatile("" : "+v"(nkh));
 #pragma unroll
@@ -700,7 +783,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
         wait_vm_barrier<KMIN + VMIN>();
       else
         wait_vm_barrier<0>();
-      if (t + 2 < n_tiles) nk_k[st] = issue_k(st);
+      if (t + 2 < n_tiles) {
+        nk_k[st] = issue_k(st);
+        k0_k[st] = key0;
+      }
     }
 
     // ---- O^T += V^T P^T over keys 0..31 while P of keys 32..63 is formed
@@ -716,15 +802,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 #pragma unroll
       for (int mb = 0; mb < MBLK; ++mb)
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[stp * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
-    lsum = exp_half(s1, pb[2], pb[3]);
+    if constexpr (MASKED) {
+      lsum = exp_half(s1, follow_max(s1), pb[2], pb[3]);
+    } else {
+      lsum = exp_half(s1, m_run, pb[2], pb[3]);
 #pragma unroll
-    for (int i = 0; i < 2 * MBLK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * MBLK), 0);
-    }
-    if (__any(lsum > 0x1p60f)) {
-      raise_by(fmaxf(max_half(s1) - m_run, 0.f));
-      lsum = exp_half(s1, pb[2], pb[3]);
+      for (int i = 0; i < 2 * MBLK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * MBLK), 0);
+      }
+      if (__any(lsum > 0x1p60f)) {
+        raise_by(fmaxf(max_half(s1) - m_run, 0.f));
+        lsum = exp_half(s1, m_run, pb[2], pb[3]);
+      }
     }
     l_run += lsum;
     // ---- O^T += V^T P^T over keys 32..63
@@ -760,7 +850,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 // queries and loads run two tiles ahead).  The larger one runs about 10% faster per query once
 // the grid fills the chip; with few query tiles its coarser grid leaves CUs idle, so pick by
 // the number of dispatch rounds each needs on 256 CUs.
-hipError_t launch_attention_bf16_vt(const AttnBatch& a, int D, hipStream_t stream) {
+template <bool MASKED>
+static hipError_t launch_vt(const AttnBatch& a, int D, hipStream_t stream) {
   const AttnArgs& a0 = a.b[0];
   const int64_t wg4 = (int64_t)((a0.Lq + 127) / 128) * a0.H * a.nb, wg8 = (int64_t)((a0.Lq + 255) / 256) * a0.H * a.nb;
   const double rounds4 = (double)((wg4 + 511) / 512), rounds8 = 0.9 * (double)((wg8 + 255) / 256);
@@ -770,13 +861,19 @@ hipError_t launch_attention_bf16_vt(const AttnBatch& a, int D, hipStream_t strea
   const bool big = forced == 8 || (forced != 4 && rounds8 < rounds4);
   const dim3 grid((unsigned)(big ? wg8 : wg4));
   switch (D * (big ? -1 : 1)) {
-    case 64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 4, 2>), grid, dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 4, 2>), grid, dim3(256), 0, stream, a); break;
-    case -64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 8, 4>), grid, dim3(512), 0, stream, a); break;
-    case -128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 8, 4>), grid, dim3(512), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 4, 2, MASKED>), grid, dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 4, 2, MASKED>), grid, dim3(256), 0, stream, a); break;
+    case -64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 8, 4, MASKED>), grid, dim3(512), 0, stream, a); break;
+    case -128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 8, 4, MASKED>), grid, dim3(512), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attention_bf16_vt(const AttnBatch& a, int D, hipStream_t stream) { return launch_vt<false>(a, D, stream); }
+
+hipError_t launch_attention_bf16_masked(const AttnBatch& a, int D, hipStream_t stream) {
+  return launch_vt<true>(a, D, stream);
 }
 
 }  // namespace skv

@@ -58,6 +58,10 @@ struct AttnArgs {
   int32_t nseg;
   int32_t Lq, H;
   float sl2;       // softmax scale * log2(e)
+  // many chunks at once under the sink + window block-causal mask (masked kernel only):
+  // frames of mF tokens, query frames from mq0 in chunks of mc frames, mS sinks, window mW;
+  // seg[0] then describes the keys / V^T of the whole sequence
+  int32_t mF, mq0, mc, mS, mW;
 };
 
 // Up to kMaxAttnBatch independent attention problems of one shape (same Lq, H, D) in one

@@ -62,6 +62,7 @@ hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream);
 // softmax(q K^T * scale) V over the concatenated key ranges of a.seg.
 // bf16, V transposed (cache path) / V token-major (cross attention); fp32 takes any V strides.
 hipError_t launch_attention_bf16_vt(const AttnBatch& ab, int D, hipStream_t stream);
+hipError_t launch_attention_bf16_masked(const AttnBatch& ab, int D, hipStream_t stream);
 hipError_t launch_attention_bf16_tokv(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, int D, hipStream_t stream);
 

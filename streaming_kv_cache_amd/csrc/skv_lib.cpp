@@ -421,6 +421,79 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
   return e == hipSuccess ? SKV_OK : SKV_ERR_HIP;
 }
 
+// Many-chunk attention: checks shared by the size query and the call.
+static skv_status block_causal_geometry(const skv_config* cfg, int32_t n_frames, int32_t q_frame0,
+                                        skv::Geometry* g, int64_t* row_pad) {
+  skv_status st = skv::make_geometry(cfg, g);
+  if (st != SKV_OK) return st;
+  if (g->dtype != SKV_BF16) return SKV_ERR_CONFIG;
+  if (n_frames < 1) return SKV_ERR_SHAPE;
+  // q_frame0 < 0: size query only (no query frames to check)
+  if (q_frame0 >= 0 && (q_frame0 >= n_frames || (n_frames - q_frame0) % g->c)) return SKV_ERR_SHAPE;
+  const int64_t keys = (int64_t)n_frames * g->F;
+  *row_pad = (keys + 63) / 64 * 64;
+  // 32-bit offsets inside one head's key rows (token-major) and V^T rows
+  if ((keys + 64) * g->H * g->D * g->elt > INT32_MAX || (int64_t)g->D * *row_pad * g->elt > INT32_MAX ||
+      keys > INT32_MAX / 2)
+    return SKV_ERR_SHAPE;
+  return SKV_OK;
+}
+
+skv_status block_causal_workspace_bytes(const skv_config* cfg, int32_t n_frames, size_t* bytes) {
+  if (!bytes) return SKV_ERR_NULL;
+  skv::Geometry g;
+  int64_t row_pad = 0;
+  const skv_status st = block_causal_geometry(cfg, n_frames, -1, &g, &row_pad);
+  if (st != SKV_OK) return st;
+  *bytes = (size_t)g.H * g.D * row_pad * g.elt;
+  return SKV_OK;
+}
+
+skv_status block_causal_attention(const skv_config* cfg, const void* q, const void* k, const void* v,
+                                  int32_t n_frames, int32_t q_frame0, void* workspace, void* out, void* stream) {
+  skv_status st;
+  for (const void* p : {q, k, v, (const void*)workspace, (const void*)out})
+    if ((st = check_ptr(p)) != SKV_OK) return st;
+  skv::Geometry g;
+  int64_t row_pad = 0;
+  if (q_frame0 < 0) return SKV_ERR_SHAPE;
+  if ((st = block_causal_geometry(cfg, n_frames, q_frame0, &g, &row_pad)) != SKV_OK) return st;
+  // values -> V^T rows of the whole sequence in the workspace
+  skv::WriteArgs wa{};
+  wa.k_src = nullptr;
+  wa.v_src = v;
+  wa.tok_stride = (int64_t)g.H * g.D;
+  wa.head_stride = g.D;
+  wa.vt_dst = workspace;
+  wa.vt_hs = (int64_t)g.D * row_pad;
+  wa.vt_ds = row_pad;
+  wa.nruns = 0;
+  wa.F = g.F;
+  wa.H = g.H;
+  wa.D = g.D;
+  wa.n_tok = n_frames * g.F;
+  wa.row_pad = (int32_t)row_pad;
+  if (skv::launch_write_kv(wa, g.elt, (hipStream_t)stream) != hipSuccess) return SKV_ERR_HIP;
+  skv::AttnBatch ab{};
+  ab.nb = 1;
+  skv::AttnArgs& a = ab.b[0];
+  a.q = q;
+  a.out = out;
+  a.Lq = (n_frames - q_frame0) * g.F;
+  a.H = g.H;
+  a.sl2 = softmax_scale_log2(g.D);
+  a.nseg = 1;
+  a.seg[0] = skv::KvSeg{k, workspace, (int64_t)g.D, (int64_t)g.H * g.D, (int64_t)g.D * row_pad, 1, row_pad,
+                        n_frames * g.F, 1};
+  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  a.mF = g.F;
+  a.mq0 = q_frame0;
+  a.mc = g.c;
+  a.mS = g.S;
+  a.mW = g.W;
+  return skv::launch_attention_bf16_masked(ab, g.D, (hipStream_t)stream) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+}
+
 skv_status sampler_step(const void* x_t, const void* v_cond, const void* v_uncond, double cfg_scale,
                         const void* noise, int64_t n, double sigma, double sigma_next, int32_t dtype, void* x0_out,
                         void* x_next_out, void* stream) {

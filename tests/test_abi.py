@@ -171,3 +171,26 @@ def test_chunk_attention_batch_validation():
     assert f(arr(h1, h2), 2, two, two, two, 3, two, nul) == skv.ERR_SHAPE
     for h in (h1, h2, h3):
         skv.lib.kv_cache_destroy(h)
+
+
+def test_block_causal_validation():
+    """Size query and argument checks of block_causal_attention (no GPU work reaches a launch)."""
+    V = ctypes.c_void_p
+    p, nul = V(0x40000), V(0)
+    c = LB480.c_struct()
+    b = ctypes.c_size_t()
+    assert skv.lib.block_causal_workspace_bytes(ctypes.byref(c), 88, ctypes.byref(b)) == skv.OK
+    assert b.value == 40 * 128 * ((88 * 1560 + 63) // 64 * 64) * 2
+    assert skv.lib.block_causal_workspace_bytes(ctypes.byref(c), 0, ctypes.byref(b)) == skv.ERR_SHAPE
+    assert skv.lib.block_causal_workspace_bytes(ctypes.byref(c), 88, None) == skv.ERR_NULL
+    f = skv.lib.block_causal_attention
+    assert f(ctypes.byref(c), nul, p, p, 88, 0, p, p, nul) == skv.ERR_NULL
+    assert f(ctypes.byref(c), p, p, p, 88, 0, V(0x40008), p, nul) == skv.ERR_ALIGN
+    assert f(ctypes.byref(c), p, p, p, 87, 0, p, p, nul) == skv.ERR_SHAPE        # not whole chunks
+    assert f(ctypes.byref(c), p, p, p, 88, 88, p, p, nul) == skv.ERR_SHAPE       # no query frames
+    assert f(ctypes.byref(c), p, p, p, 88, -1, p, p, nul) == skv.ERR_SHAPE
+    assert f(ctypes.byref(c), p, p, p, 2000, 0, p, p, nul) == skv.ERR_SHAPE      # past 32-bit head offsets
+    f32 = skv.Config(2, 64, 4, 4, 2, 1, 4, skv.ROPE_ABS, skv.F32).c_struct()
+    assert f(ctypes.byref(f32), p, p, p, 8, 0, p, p, nul) == skv.ERR_CONFIG      # bf16 only
+    ab = ABOT.c_struct()
+    assert skv.lib.block_causal_workspace_bytes(ctypes.byref(ab), 5 + 3 * 7, ctypes.byref(b)) == skv.OK
