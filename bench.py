@@ -34,9 +34,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="abot720")
+    ap.add_argument("--fused-rope", action="store_true",
+                    help="library-side rotation (raw q/k in, keys stored at absolute ids, no REL window pass); "
+                         "chunk_attention's time then includes its q/k rotation launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--pool", type=int, default=2, help="device-resident input sets cycled over steps")
+    ap.add_argument("--bc-chunks", type=int, default=None,
+                    help="query chunks of the many-chunk block-causal leg after the prefill frames "
+                         "(default: the workload's chunk count, at most 22)")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy the cache out once (plain row copies of known size) so that "
                          "counter passes can scale FETCH_SIZE / WRITE_SIZE")
@@ -58,6 +64,8 @@ class Runner:
         cfg = wl.cfg
         self.cfg = cfg
         self.rel = cfg.rope_mode == skv.ROPE_REL
+        # fused rotation: raw q / k everywhere, the library rotates (the keys at absolute ids)
+        self.fused = bool(cfg.fused_rope)
         self.caches = [skv.KVCache(cfg) for _ in range(wl.layers)]
         c, f, h, d = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim
         shape = (c * f, h, d)
@@ -96,7 +104,7 @@ class Runner:
         sk = si.draw(shape, 0, 0, 0, si.SINK_K, cfg.torch_dtype).cuda()
         sv = si.draw(shape, 0, 0, 0, si.SINK_V, cfg.torch_dtype).cuda()
         for cache in self.caches:
-            k = sk if self.rel else cache.rope_apply(sk, start_frame=0)
+            k = sk if self.rel or self.fused else cache.rope_apply(sk, start_frame=0)
             cache.append_evict(k, sv)
 
     def _ev(self, kind):
@@ -110,7 +118,7 @@ class Runner:
         wl = self.wl
         sets = self.pool[self.chunk % len(self.pool)]
         self._ev("step0")
-        if self.rel:
+        if self.rel and not self.fused:
             self._ev("win0")
             for cache in self.caches:
                 cache.rope_apply_window()
@@ -120,22 +128,29 @@ class Runner:
             q, k, v, noise = sets[p]
             for li, cache in enumerate(self.caches):
                 t = cache.info().n_appended
-                self._ev("rope0")
-                cache.rope_apply(q, out=self.qr, start_frame=t)
-                cache.rope_apply(k, out=self.kr[li], start_frame=t)
-                self._ev("rope1")
-                self._ev("stage0")
-                cache.stage_v(v)
-                self._ev("attn0")
-                cache.chunk_attention(self.qr, self.kr[li], None, out=self.out)
-                self._ev("attn1")
+                if self.fused:
+                    self._ev("stage0")
+                    cache.stage_v(v)
+                    self._ev("attn0")
+                    cache.chunk_attention(q, k, None, out=self.out)   # rotates q and k first
+                    self._ev("attn1")
+                else:
+                    self._ev("rope0")
+                    cache.rope_apply(q, out=self.qr, start_frame=t)
+                    cache.rope_apply(k, out=self.kr[li], start_frame=t)
+                    self._ev("rope1")
+                    self._ev("stage0")
+                    cache.stage_v(v)
+                    self._ev("attn0")
+                    cache.chunk_attention(self.qr, self.kr[li], None, out=self.out)
+                    self._ev("attn1")
                 if wl.text_tokens:
                     self._ev("cross0")
                     self.skv.cross_attention(q, self.text[0], self.text[1], out=self.xout)
                     self._ev("cross1")
                 if p == wl.passes - 1:
                     self._ev("app0")
-                    cache.append_evict(k if self.rel else self.kr[li], v)
+                    cache.append_evict(k if self.rel or self.fused else self.kr[li], v)
                     self._ev("app1")
             if p < len(steps):
                 # few-step sampler: x0 from the velocity; re-noise to the next step unless last
@@ -152,7 +167,7 @@ class Runner:
         """Advance the cache by one chunk (write-back only): builds the steady state without attention."""
         _, k, v, _ = self.pool[self.chunk % len(self.pool)][self.wl.passes - 1]
         for li, cache in enumerate(self.caches):
-            kk = k if self.rel else cache.rope_apply(k, out=self.kr[li], start_frame=cache.info().n_appended)
+            kk = k if self.rel or self.fused else cache.rope_apply(k, out=self.kr[li], start_frame=cache.info().n_appended)
             cache.append_evict(kk, v)
         self.chunk += 1
 
@@ -214,6 +229,86 @@ def cpu_baseline(runner, target_s):
                       f"fp64 NumPy incl. RoPE of the visible keys; {reps} call(s), {total:.1f} s"}
 
 
+def block_causal_leg(runner, args):
+    """Many-chunk masked attention over a training-length sequence of this workload's shape:
+    the prefill frames plus args.bc_chunks chunks; flops count visible (query, key) pairs only."""
+    import torch
+    skv, si, cfg, wl = runner.skv, runner.si, runner.cfg, runner.wl
+    f, c, h, d = cfg.tokens_per_frame, cfg.chunk_frames, cfg.heads, cfg.head_dim
+    q0 = wl.prefill
+    nch = args.bc_chunks or min(wl.n_chunks, 22)
+    n = q0 + c * nch
+    k = si.draw((n * f, h, d), 0, 0, 0, si.K, cfg.torch_dtype).cuda()
+    v = si.draw((n * f, h, d), 0, 0, 0, si.V, cfg.torch_dtype).cuda()
+    q = si.draw(((n - q0) * f, h, d), 0, 0, 0, si.Q, cfg.torch_dtype).cuda()
+    ws = torch.empty(skv.block_causal_workspace_bytes(cfg, n), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    # query frame of chunk kk (end e) sees min(e, W) frames: the sinks and the window up to e
+    pairs = sum(c * f * min(q0 + c * (kk + 1), cfg.window_frames) * f for kk in range(nch))
+    flop = 4.0 * pairs * d * h
+    for _ in range(3):
+        skv.block_causal_attention(cfg, q, k, v, q_frame0=q0, out=out, workspace=ws)
+    evs = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        skv.block_causal_attention(cfg, q, k, v, q_frame0=q0, out=out, workspace=ws)
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return {"n_frames": n, "q_frame0": q0, "chunks": nch, "avg_ms": round(ms, 4),
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 2), "frac_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "note": "includes the V transpose into the workspace; flops of visible pairs only"}
+
+
+def guidance_leg(runner):
+    """The conditional and unconditional caches of guidance in one chunk_attention_batch launch versus
+    two chunk_attention launches, both caches at the steady window."""
+    import torch
+    skv, si, cfg, wl = runner.skv, runner.si, runner.cfg, runner.wl
+    caches = [skv.KVCache(cfg) for _ in range(2)]
+    f = cfg.tokens_per_frame
+    for cc in caches:
+        if wl.prefill:
+            shape = (wl.prefill * f, cfg.heads, cfg.head_dim)
+            sk = si.draw(shape, 0, 0, 0, si.SINK_K, cfg.torch_dtype).cuda()
+            sv = si.draw(shape, 0, 0, 0, si.SINK_V, cfg.torch_dtype).cuda()
+            cc.append_evict(sk if runner.rel or runner.fused else cc.rope_apply(sk, start_frame=0), sv)
+        for ch in range(wl.steady_chunk + 1):
+            _, kk, vv, _ = runner.pool[ch % len(runner.pool)][wl.passes - 1]
+            cc.append_evict(kk if runner.rel or runner.fused else cc.rope_apply(kk, start_frame=cc.info().n_appended), vv)
+        if runner.rel and not runner.fused:
+            cc.rope_apply_window()
+    q, k, v, _ = runner.pool[0][0]
+    for cc in caches:
+        cc.stage_v(v)
+    qs, ks = [q, q], [k, k]
+    outs = [torch.empty_like(q), torch.empty_like(q)]
+    for _ in range(3):
+        skv.chunk_attention_batch(caches, qs, ks, None, outs)
+    t = {}
+    for mode in ("batch", "single"):
+        evs = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if mode == "batch":
+                skv.chunk_attention_batch(caches, qs, ks, None, outs)
+            else:
+                for i, cc in enumerate(caches):
+                    cc.chunk_attention(qs[i], ks[i], None, out=outs[i])
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t[mode] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    n_vis = caches[0].info().n_vis
+    flop = 2 * 4.0 * cfg.chunk_frames * f * n_vis * f * cfg.head_dim * cfg.heads
+    return {"caches": 2, "n_vis": n_vis, "batch_ms": round(t["batch"], 4), "two_calls_ms": round(t["single"], 4),
+            "batch_tflops": round(flop / (t["batch"] * 1e-3) / 1e12, 2),
+            "two_calls_tflops": round(flop / (t["single"] * 1e-3) / 1e12, 2)}
+
+
 def traffic_from_profile(wl_name, per_launch_algo_bytes):
     """HBM bytes per attention launch from committed rocprofv3 counters, if taken on the current kernel."""
     p = os.path.join(ROOT, "profiles", f"attn_bf16_{wl_name}_counters.json")
@@ -235,6 +330,9 @@ def main():
     from streaming_kv_cache_amd.workloads import WORKLOADS
     import streaming_kv_cache_amd as skv
     wl = WORKLOADS[args.workload]
+    if args.fused_rope:
+        import dataclasses
+        wl = dataclasses.replace(wl, cfg=dataclasses.replace(wl.cfg, fused_rope=True))
     cfg = wl.cfg
     torch.cuda.set_device(0)
     r = Runner(wl, max(1, args.pool))
@@ -291,7 +389,8 @@ def main():
         "data": "synthetic: seeded N(0,1) q/k/v (torch CPU generator, RNE to bf16), device-resident",
         "config": {"workload": wl.name, "heads": h, "head_dim": d, "tokens_per_frame": f, "chunk_frames": c,
                    "sink_frames": cfg.sink_frames, "window_frames": cfg.window_frames, "lq": lq, "lkv": lkv,
-                   "rope": "relative" if r.rel else "absolute", "layers": wl.layers, "passes_per_chunk": wl.passes,
+                   "rope": "relative" if r.rel else "absolute", "fused_rope": r.fused,
+                   "layers": wl.layers, "passes_per_chunk": wl.passes,
                    "text_tokens": wl.text_tokens},
         "roofline": roof,
         "chunk_attention": {"tflops": round(attn_tflops, 2), "frac_peak": round(attn_tflops / peak, 4),
@@ -299,23 +398,29 @@ def main():
         "cache_update": {"GB/s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1),
                          "frac_hbm": round(app_bytes / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "avg_us": round(app_ms * 1e3, 2), "bytes": app_bytes},
-        "rope_qk": {"GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1), "avg_us": round(rope_ms * 1e3, 2)},
         "stage_v": {"GB/s": round(2 * lq * h * d * elt / (stage_ms * 1e-3) / 1e9, 1), "avg_us": round(stage_ms * 1e3, 2)},
         "per_chunk_ms": {"mean": round(float(np.mean(steps_ms)), 4), "p50": round(float(np.median(steps_ms)), 4),
                          "p99": round(float(np.percentile(steps_ms, 99)), 4)},
     }
+    if not r.fused:
+        out["rope_qk"] = {"GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1), "avg_us": round(rope_ms * 1e3, 2)}
+    else:
+        out["chunk_attention"]["note"] = "fused rotation: includes the q / k rotation launches before the kernel"
     if wl.timesteps:
         # per call: x_t, velocity and noise read, x0 and the re-noised latent written (last step: x0 only)
         ns = len(wl.timesteps)
         samp_bytes = ((ns - 1) * 5 + 3) / ns * lq * h * d * elt
         out["sampler"] = {"GB/s": round(samp_bytes / (samp_ms * 1e-3) / 1e9, 1), "avg_us": round(samp_ms * 1e3, 2),
                           "timesteps": list(wl.timesteps)}
-    if r.rel:
+    if r.rel and not r.fused:
         win_bytes = 2 * (cfg.window_frames - c) * f * h * d * elt
         out["rope_window"] = {"GB/s": round(win_bytes / (win_ms * 1e-3) / 1e9, 1), "avg_us": round(win_ms * 1e3, 2)}
     if wl.text_tokens:
         xf = 4.0 * lq * wl.text_tokens * d * h
         out["cross_attention"] = {"tflops": round(xf / (cross_ms * 1e-3) / 1e12, 2), "avg_ms": round(cross_ms, 4)}
+    if bf16 and wl.layers == 1:
+        out["block_causal"] = block_causal_leg(r, args)
+        out["guidance_batch"] = guidance_leg(r)
     if not args.no_cpu_baseline and wl.layers == 1:
         out["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 1
+#define SKV_ABI_VERSION 2
 
 typedef enum {
   SKV_OK = 0,
@@ -70,7 +70,20 @@ typedef struct {
   double rope_theta;            /* rotary base; 0 -> 10000 */
   int32_t rope_mode;            /* skv_rope_mode */
   int32_t dtype;                /* skv_dtype of every tensor the handle touches */
+  int32_t fused_rope;           /* 0: the protocol above; 1: the library rotates (see below) */
 } skv_config;
+
+/* fused_rope = 1: callers pass UN-rotated q and k everywhere; rope_apply_window is
+ * not used (SKV_ERR_STATE).  kv_cache_append_evict rotates k at each frame's
+ * absolute id f while writing it (both modes), chunk_attention rotates q and
+ * k_cur itself (into the workspace) before attending.  REL keeps its meaning: a
+ * score depends only on the difference of the two time ids, and for ring and
+ * current-chunk keys the slot-index difference equals the frame-number
+ * difference, so those are attended with queries rotated at absolute ids
+ * (start frame T + i); only the sink frames, whose slot ids are their frame
+ * numbers, need the queries at their slot ids n_vis - c + i.  The window is
+ * therefore never rotated again after the write-back (no per-chunk window pass,
+ * no window workspace); kv_cache_gather returns keys rotated at absolute ids. */
 
 typedef struct {
   int64_t n_appended;   /* frames appended since init/reset (T) */

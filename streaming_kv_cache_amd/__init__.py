@@ -36,7 +36,7 @@ class SkvConfig(ctypes.Structure):
         ("chunk_frames", ctypes.c_int32), ("sink_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
         ("rope_t", ctypes.c_int32), ("rope_h", ctypes.c_int32), ("rope_w", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
-        ("rope_mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("rope_mode", ctypes.c_int32), ("dtype", ctypes.c_int32), ("fused_rope", ctypes.c_int32),
     ]
 
 
@@ -135,6 +135,7 @@ class Config:
     dtype: int = BF16
     rope_split: tuple = (0, 0, 0)
     rope_theta: float = 0.0
+    fused_rope: bool = False   # callers pass raw q/k; the library rotates (see skv.h)
 
     @property
     def tokens_per_frame(self) -> int:
@@ -148,7 +149,7 @@ class Config:
         t, h, w = self.rope_split
         return SkvConfig(self.heads, self.head_dim, self.grid_h, self.grid_w, self.chunk_frames,
                          self.sink_frames, self.window_frames, t, h, w, float(self.rope_theta),
-                         int(self.rope_mode), int(self.dtype))
+                         int(self.rope_mode), int(self.dtype), int(bool(self.fused_rope)))
 
 
 def cache_bytes(cfg: Config):

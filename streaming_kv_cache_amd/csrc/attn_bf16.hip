@@ -404,10 +404,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 
   // Q^T, pre-multiplied by softmax scale * log2(e): scores come out in log2 units.
   bf16x8_t qreg[KSTEPS];
-  {
+  auto load_q = [&](const void* src) {
     const int qi = q_base + l32;
     const bool ok = qi < a.Lq;
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)(ok ? qi : 0) * a.H + h) * D + 8 * hf;
+    const uint16_t* qp = (const uint16_t*)src + ((int64_t)(ok ? qi : 0) * a.H + h) * D + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       u32x4_t v = ok ? *(const u32x4_t*)(qp + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
@@ -415,7 +415,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(bf16_lo_to_f32(v[e]) * sl2, bf16_hi_to_f32(v[e]) * sl2);
       qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
-  }
+  };
+  load_q(a.q);
   f32x16_t o[MBLK];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb)
@@ -467,8 +468,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   // Two uniform tile iterators over the key ranges: K runs ahead of V.
   auto seg_n = [&](int s_) -> int { return MASKED ? (s_ == 0 ? sink_keys : ring_keys) : a.seg[s_].n; };
   auto seg_start = [&](int s_) -> int { return MASKED ? (s_ == 0 ? 0 : ring0) : 0; };
-  int n_tiles = 0;
-  for (int s_ = 0; s_ < nseg; ++s_) n_tiles += (seg_n(s_) + kBN - 1) / kBN;
+  int n_tiles = 0, alt_tiles = 1 << 30;  // tiles before the ranges that use the queries at q_alt
+  for (int s_ = 0; s_ < nseg; ++s_) {
+    if (!MASKED && s_ == a.alt_seg) alt_tiles = n_tiles;
+    n_tiles += (seg_n(s_) + kBN - 1) / kBN;
+  }
   if (n_tiles == 0) return;  // no keys: the host never launches this
   int ksi = 0, krem = 0, k_rs_b = 0;
   const uint8_t* kp = nullptr;
@@ -717,6 +721,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       }
     }
 
+    if (t == alt_tiles) load_q(a.q_alt);
     const uint8_t* kt = smem + st * KT_B;
     // ---- keys 0..31: S'^T = K (Q^T * scale * log2 e)
     // all LDS reads of a product are issued before its first MFMA (sched_barrier keeps them there)

@@ -34,6 +34,17 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
   float m = -INFINITY, l = 0.f;
   for (int si = 0; si < a.nseg; ++si) {
+    if (si == a.alt_seg) {  // ranges from here on use the queries at q_alt
+      const float* qa = (const float*)a.q_alt + ((int64_t)qi * a.H + h) * D;
+#pragma unroll
+      for (int d = 0; d < D; d += 4) {
+        f32x4_t v = q_ok ? *(const f32x4_t*)(qa + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        q[d] = v[0] * a.sl2;
+        q[d + 1] = v[1] * a.sl2;
+        q[d + 2] = v[2] * a.sl2;
+        q[d + 3] = v[3] * a.sl2;
+      }
+    }
     const KvSeg sg = a.seg[si];
     const float* kb = (const float*)sg.k + h * sg.k_hs;
     const float* vb = (const float*)sg.v + h * sg.v_hs;

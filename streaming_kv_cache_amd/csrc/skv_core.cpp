@@ -43,6 +43,8 @@ skv_status make_geometry(const skv_config* cfg, Geometry* g) {
     if (cur > lim || kst > lim || vst > lim) return SKV_ERR_CONFIG;
   }
   if (cfg->rope_mode != SKV_ROPE_ABS && cfg->rope_mode != SKV_ROPE_REL) return SKV_ERR_CONFIG;
+  if (cfg->fused_rope != 0 && cfg->fused_rope != 1) return SKV_ERR_CONFIG;
+  r.fused = cfg->fused_rope;
   r.mode = cfg->rope_mode;
   if (cfg->rope_t == 0 && cfg->rope_h == 0 && cfg->rope_w == 0) {
     int32_t hw = 2 * (r.D / 6);

@@ -30,6 +30,7 @@ struct Geometry {
   int32_t mode = SKV_ROPE_ABS;
   int32_t dtype = SKV_F32;
   int32_t elt = 4;                       // bytes per element
+  int32_t fused = 0;                     // fused_rope: the library rotates q / k
 };
 
 // Check *cfg and fill the derived geometry (default split / theta applied).
@@ -39,8 +40,9 @@ skv_status make_geometry(const skv_config* cfg, Geometry* g);
 bool attention_head_dim_supported(int32_t dtype, int32_t D);
 
 inline int64_t store_elems(const Geometry& g) { return (int64_t)g.W * g.F * g.H * g.D; }
+// REL window keys rotated once per chunk (not used with fused rotation).
 inline int64_t workspace_elems(const Geometry& g) {
-  return g.mode == SKV_ROPE_REL ? (int64_t)(g.W - g.c) * g.F * g.H * g.D : 0;
+  return g.mode == SKV_ROPE_REL && !g.fused ? (int64_t)(g.W - g.c) * g.F * g.H * g.D : 0;
 }
 
 // One contiguous run of visible history frames in physical slots, together with

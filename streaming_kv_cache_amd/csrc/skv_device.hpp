@@ -58,6 +58,9 @@ struct AttnArgs {
   int32_t nseg;
   int32_t Lq, H;
   float sl2;       // softmax scale * log2(e)
+  // key ranges from seg[alt_seg] on are attended with the queries at q_alt (same layout as q)
+  const void* q_alt;
+  int32_t alt_seg;
   // many chunks at once under the sink + window block-causal mask (masked kernel only):
   // frames of mF tokens, query frames from mq0 in chunks of mc frames, mS sinks, window mW;
   // seg[0] then describes the keys / V^T of the whole sequence

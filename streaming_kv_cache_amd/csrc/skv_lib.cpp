@@ -60,10 +60,21 @@ float softmax_scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt(
 int64_t vt_row(const skv::Geometry& g) { return (int64_t)g.W * g.F; }
 // Current-chunk V^T rows in the workspace: c*F keys padded to a multiple of 64.
 int64_t cur_row(const skv::Geometry& g) { return ((int64_t)g.c * g.F + 63) / 64 * 64; }
-// Workspace: [REL window keys, (W-c)*F*H*D] then [current-chunk V^T, H*D*cur_row].
+// Workspace: [REL window keys, (W-c)*F*H*D (not with fused rotation)]
+//            [fused rotation: q at absolute ids, q at slot ids (REL), k_cur at absolute ids; c*F*H*D each]
+//            [current-chunk V^T, H*D*cur_row].
 int64_t ws_window_elems(const skv::Geometry& g) { return skv::workspace_elems(g); }
-int64_t ws_total_elems(const skv::Geometry& g) { return ws_window_elems(g) + (int64_t)g.H * g.D * cur_row(g); }
-void* ws_vt(const skv_cache* c) { return (char*)c->ws + ws_window_elems(c->g) * c->g.elt; }
+int64_t chunk_elems(const skv::Geometry& g) { return (int64_t)g.c * g.F * g.H * g.D; }
+int64_t ws_fused_elems(const skv::Geometry& g) {
+  return g.fused ? chunk_elems(g) * (g.mode == SKV_ROPE_REL ? 3 : 2) : 0;
+}
+int64_t ws_total_elems(const skv::Geometry& g) {
+  return ws_window_elems(g) + ws_fused_elems(g) + (int64_t)g.H * g.D * cur_row(g);
+}
+void* ws_q_abs(const skv_cache* c) { return (char*)c->ws + ws_window_elems(c->g) * c->g.elt; }
+void* ws_k_cur(const skv_cache* c) { return (char*)ws_q_abs(c) + chunk_elems(c->g) * c->g.elt; }
+void* ws_q_rel(const skv_cache* c) { return (char*)ws_k_cur(c) + chunk_elems(c->g) * c->g.elt; }
+void* ws_vt(const skv_cache* c) { return (char*)c->ws + (ws_window_elems(c->g) + ws_fused_elems(c->g)) * c->g.elt; }
 
 // Current chunk's V -> V^T rows in the workspace (tail zero-filled to a multiple of 64 keys).
 skv_status stage_v(skv_cache* c, const void* v_cur, void* stream) {
@@ -83,6 +94,48 @@ skv_status stage_v(skv_cache* c, const void* v_cur, void* stream) {
   wa.n_tok = g.c * g.F;
   wa.row_pad = (int32_t)cur_row(g);
   return launched(c, skv::launch_write_kv(wa, g.elt, (hipStream_t)stream));
+}
+
+// Rotary launch over n_frames frames of a token-major tensor (or the store, via runs).
+skv::RopeLaunch rope_launch(const skv::Geometry& g, skv::TokView src, skv::TokView dst, int32_t n_frames,
+                            int64_t t0, int64_t clamp_max) {
+  skv::RopeLaunch L;
+  L.src = src;
+  L.dst = dst;
+  L.runs[0] = skv::FrameRun{0, n_frames, 0, 0};
+  L.nruns = 1;
+  L.n_frames = n_frames;
+  L.F = g.F;
+  L.gw = g.gw;
+  L.H = g.H;
+  L.D = g.D;
+  L.rope_t = g.rope_t;
+  L.rope_h = g.rope_h;
+  L.rope_w = g.rope_w;
+  L.theta = g.theta;
+  L.t0 = t0;
+  L.clamp_max = clamp_max;
+  L.dtype_bf16 = g.dtype == SKV_BF16;
+  return L;
+}
+
+// Fused rotation before an attention pass: q at absolute ids (and at slot ids for REL sinks),
+// k_cur at absolute ids, into the workspace.
+skv_status fused_prepare(skv_cache* c, const void* q, const void* k_cur, void* stream) {
+  const skv::Geometry& g = c->g;
+  const skv::VisiblePlan p = c->ring.plan(g, g.c);
+  const int64_t T = c->ring.T;
+  skv_status st = launched(c, skv::launch_rope(rope_launch(g, token_view(g, q), token_view(g, ws_q_abs(c)), g.c, T, -1),
+                                               (hipStream_t)stream));
+  if (st != SKV_OK) return st;
+  if (g.mode == SKV_ROPE_REL && p.n_sink_vis > 0) {
+    st = launched(c, skv::launch_rope(rope_launch(g, token_view(g, q), token_view(g, ws_q_rel(c)), g.c,
+                                                  p.n_vis - g.c, g.W - 1),
+                                      (hipStream_t)stream));
+    if (st != SKV_OK) return st;
+  }
+  return launched(c, skv::launch_rope(rope_launch(g, token_view(g, k_cur), token_view(g, ws_k_cur(c)), g.c, T, -1),
+                                      (hipStream_t)stream));
 }
 
 }  // namespace
@@ -190,8 +243,16 @@ skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int
       runs[nruns++] = skv::FrameRun{i, 1, i, slot};
     }
   }
+  if (g.fused) {
+    // k rotated at the frames' absolute ids straight into their slots; V below
+    skv::RopeLaunch L = rope_launch(g, token_view(g, k), store_view(g, c->k_store), n_frames, c->ring.T, -1);
+    L.nruns = nruns;
+    for (int i = 0; i < 3; ++i) L.runs[i] = i < nruns ? runs[i] : skv::FrameRun{0, 0, 0, 0};
+    st = launched(c, skv::launch_rope(L, (hipStream_t)stream));
+    if (st != SKV_OK) return st;
+  }
   skv::WriteArgs wa{};
-  wa.k_src = k;
+  wa.k_src = g.fused ? nullptr : k;
   wa.v_src = v;
   wa.tok_stride = (int64_t)g.H * g.D;
   wa.head_stride = g.D;
@@ -224,21 +285,7 @@ skv_status rope_apply(const skv_cache* cc, const void* x_in, void* x_out, int32_
   if ((st = check_ptr(x_out)) != SKV_OK) return st;
   const skv::Geometry& g = c->g;
   if (n_frames < 1 || (int64_t)n_frames * g.F > (int64_t)INT32_MAX / 2) return SKV_ERR_SHAPE;
-  skv::RopeLaunch L;
-  L.src = token_view(g, x_in);
-  L.dst = token_view(g, x_out);
-  L.runs[0] = skv::FrameRun{0, n_frames, 0, 0};
-  L.nruns = 1;
-  L.n_frames = n_frames;
-  L.F = g.F;
-  L.gw = g.gw;
-  L.H = g.H;
-  L.D = g.D;
-  L.rope_t = g.rope_t;
-  L.rope_h = g.rope_h;
-  L.rope_w = g.rope_w;
-  L.theta = g.theta;
-  L.dtype_bf16 = g.dtype == SKV_BF16;
+  skv::RopeLaunch L = rope_launch(g, token_view(g, x_in), token_view(g, x_out), n_frames, 0, -1);
   if (g.mode == SKV_ROPE_ABS) {
     if (start_frame < 0) return SKV_ERR_SHAPE;
     L.t0 = start_frame;
@@ -256,27 +303,15 @@ skv_status rope_apply_window(skv_cache* c, void* stream) {
   skv_status st = check_handle(c);
   if (st != SKV_OK) return st;
   const skv::Geometry& g = c->g;
-  if (g.mode != SKV_ROPE_REL) return SKV_ERR_STATE;
+  if (g.mode != SKV_ROPE_REL || g.fused) return SKV_ERR_STATE;
   const skv::VisiblePlan p = c->ring.plan(g, g.c);
   if (p.n_hist > 0) {
-    skv::RopeLaunch L;
-    L.src = store_view(g, c->k_store);
-    L.dst = skv::TokView{c->ws, (int64_t)g.D, (int64_t)(g.W - g.c) * g.F * g.D};
+    skv::RopeLaunch L = rope_launch(g, store_view(g, c->k_store),
+                                    skv::TokView{c->ws, (int64_t)g.D, (int64_t)(g.W - g.c) * g.F * g.D}, p.n_hist,
+                                    0, g.W - 1);
     L.nruns = p.n_runs;
     for (int i = 0; i < p.n_runs; ++i)
       L.runs[i] = skv::FrameRun{p.runs[i].logical0, p.runs[i].frames, p.runs[i].slot0, p.runs[i].logical0};
-    L.n_frames = p.n_hist;
-    L.F = g.F;
-    L.gw = g.gw;
-    L.H = g.H;
-    L.D = g.D;
-    L.rope_t = g.rope_t;
-    L.rope_h = g.rope_h;
-    L.rope_w = g.rope_w;
-    L.theta = g.theta;
-    L.t0 = 0;
-    L.clamp_max = g.W - 1;
-    L.dtype_bf16 = g.dtype == SKV_BF16;
     st = launched(c, skv::launch_rope(L, (hipStream_t)stream));
     if (st != SKV_OK) return st;
   }
@@ -297,10 +332,21 @@ static skv_status attention_args(skv_cache* c, const void* q, const void* k_cur,
   if (n_frames != g.c) return SKV_ERR_SHAPE;
   const skv::VisiblePlan p = c->ring.plan(g, g.c);
   const bool rel = g.mode == SKV_ROPE_REL;
-  if (rel && p.n_hist > 0 && !c->window_ready) return SKV_ERR_STATE;
+  if (rel && !g.fused && p.n_hist > 0 && !c->window_ready) return SKV_ERR_STATE;
   if (!v_cur && !c->v_staged) return SKV_ERR_STATE;
 
+  // fused rotation: the workspace copies written by fused_prepare; REL sinks use the queries at
+  // slot ids, everything after them the queries at absolute ids
   a->q = q;
+  a->q_alt = nullptr;
+  a->alt_seg = 1 << 20;
+  if (g.fused) {
+    const bool rel_sinks = rel && p.n_sink_vis > 0;
+    a->q = rel_sinks ? ws_q_rel(c) : ws_q_abs(c);
+    a->q_alt = ws_q_abs(c);
+    a->alt_seg = rel_sinks ? 1 : 1 << 20;
+    k_cur = ws_k_cur(c);
+  }
   a->out = out;
   a->Lq = g.c * g.F;
   a->H = g.H;
@@ -312,7 +358,7 @@ static skv_status attention_args(skv_cache* c, const void* q, const void* k_cur,
   for (int i = 0; i < p.n_runs; ++i) {
     const skv::SlotRun& r = p.runs[i];
     skv::KvSeg sg;
-    if (rel) {
+    if (rel && !g.fused) {
       sg.k = byte_ptr(c->ws, (int64_t)r.logical0 * g.F * g.D, g.elt);
       sg.k_hs = ws_hs;
     } else {
@@ -346,7 +392,7 @@ static skv_status attention_args(skv_cache* c, const void* q, const void* k_cur,
 
 static bool same_geometry(const skv::Geometry& x, const skv::Geometry& y) {
   return x.H == y.H && x.D == y.D && x.gh == y.gh && x.gw == y.gw && x.c == y.c && x.S == y.S && x.W == y.W &&
-         x.dtype == y.dtype && x.mode == y.mode;
+         x.dtype == y.dtype && x.mode == y.mode && x.fused == y.fused;
 }
 
 skv_status chunk_attention_batch(const skv_cache* const* caches, int32_t n_caches, const void* const* q,
@@ -367,13 +413,18 @@ skv_status chunk_attention_batch(const skv_cache* const* caches, int32_t n_cache
     if (st != SKV_OK) return st;
     if (!same_geometry(cs[i]->g, cs[0]->g)) return SKV_ERR_CONFIG;
   }
-  // everything checked: stage the values given, then one launch for all elements
-  for (int i = 0; i < n_caches; ++i)
+  // everything checked: rotate (fused), stage the values given, then one launch for all elements
+  for (int i = 0; i < n_caches; ++i) {
+    if (cs[i]->g.fused) {
+      const skv_status st = fused_prepare(cs[i], q[i], k_cur[i], stream);
+      if (st != SKV_OK) return st;
+    }
     if (v_cur && v_cur[i]) {
       const skv_status st = stage_v(cs[i], v_cur[i], stream);
       if (st != SKV_OK) return st;
       cs[i]->v_staged = true;
     }
+  }
   const skv::Geometry& g = cs[0]->g;
   hipError_t e = hipSuccess;
   if (g.dtype == SKV_BF16) {
@@ -406,9 +457,10 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
   if (n_q < 1 || n_text < 1 || (int64_t)n_text > (int64_t)INT32_MAX / 2 ||
       (int64_t)n_q * heads > (int64_t)INT32_MAX / 2)
     return SKV_ERR_SHAPE;
-  skv::AttnArgs a;
+  skv::AttnArgs a{};
   a.q = q;
   a.out = out;
+  a.alt_seg = 1 << 20;
   a.Lq = n_q;
   a.H = heads;
   a.sl2 = softmax_scale_log2(head_dim);
@@ -479,6 +531,7 @@ skv_status block_causal_attention(const skv_config* cfg, const void* q, const vo
   skv::AttnArgs& a = ab.b[0];
   a.q = q;
   a.out = out;
+  a.alt_seg = 1 << 20;
   a.Lq = (n_frames - q_frame0) * g.F;
   a.H = g.H;
   a.sl2 = softmax_scale_log2(g.D);

@@ -35,10 +35,19 @@ def f64(x):
     return si.to_f64(x)
 
 
+def fused(wl):
+    """The same workload with the library rotating q / k (callers pass raw tensors everywhere)."""
+    import dataclasses
+    return dataclasses.replace(wl, cfg=dataclasses.replace(wl.cfg, fused_rope=True))
+
+
 def gpu_pass(cache, q, k, v):
-    """rope(q), rope(k) at the chunk's ids, then chunk attention; returns (out, k to append, v)."""
+    """rope(q), rope(k) at the chunk's ids, then chunk attention; returns (out, k to append, v).
+    With fused rotation the raw tensors go in as they are."""
     t = cache.info().n_appended
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    if cache.cfg.fused_rope:
+        return cache.chunk_attention(qd, kd, vd), kd, vd
     qr = cache.rope_apply(qd, start_frame=t)
     kr = cache.rope_apply(kd, start_frame=t)
     out = cache.chunk_attention(qr, kr, vd)
@@ -51,7 +60,7 @@ def prefill(wl, cache, orc, base=0):
         return
     sk = draw(wl, wl.prefill, 0, 0, si.SINK_K, base)
     sv = draw(wl, wl.prefill, 0, 0, si.SINK_V, base)
-    if cache.cfg.rope_mode == skv.ROPE_ABS:
+    if cache.cfg.rope_mode == skv.ROPE_ABS and not cache.cfg.fused_rope:
         kd = cache.rope_apply(sk.cuda(), start_frame=cache.info().n_appended)
     else:
         kd = sk.cuda()
@@ -67,7 +76,7 @@ def rollout(wl, n_chunks, passes=(0, 1, 2, 3, WRITE_BACK), base=0, with_oracle=T
     orc = oracle_for(wl) if with_oracle else None
     prefill(wl, cache, orc, base)
     for ch in range(n_chunks):
-        if wl.cfg.rope_mode == skv.ROPE_REL:
+        if wl.cfg.rope_mode == skv.ROPE_REL and not wl.cfg.fused_rope:
             cache.rope_apply_window()
         for p in passes:
             q = draw(wl, wl.cfg.chunk_frames, ch, p, si.Q, base)

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert skv.lib.skv_abi_version() == 1
+    assert skv.lib.skv_abi_version() == 2
     for code in range(7):
         assert skv.status_string(code)
     assert skv.status_string(99) == "unknown status"
@@ -194,3 +194,22 @@ def test_block_causal_validation():
     assert f(ctypes.byref(f32), p, p, p, 8, 0, p, p, nul) == skv.ERR_CONFIG      # bf16 only
     ab = ABOT.c_struct()
     assert skv.lib.block_causal_workspace_bytes(ctypes.byref(ab), 5 + 3 * 7, ctypes.byref(b)) == skv.OK
+
+
+def test_fused_rope_config():
+    """fused_rope: 0/1 only; the workspace holds the rotated chunk copies instead of the REL window;
+    the window call is not used."""
+    import dataclasses
+    bad = dataclasses.replace(ABOT, fused_rope=True).c_struct()
+    bad.fused_rope = 2
+    s, w = ctypes.c_size_t(), ctypes.c_size_t()
+    assert skv.lib.kv_cache_bytes(ctypes.byref(bad), ctypes.byref(s), ctypes.byref(w)) == skv.ERR_CONFIG
+    lq_elems = 3 * 880 * 24 * 128
+    vt = 24 * 128 * ((3 * 880 + 63) // 64 * 64)
+    assert skv.cache_bytes(dataclasses.replace(ABOT, fused_rope=True))[1] == (3 * lq_elems + vt) * 2
+    assert skv.cache_bytes(dataclasses.replace(LB480, fused_rope=True))[1] == \
+        (2 * 4 * 1560 * 40 * 128 + 40 * 128 * ((4 * 1560 + 63) // 64 * 64)) * 2
+    st, h = _init(dataclasses.replace(ABOT, fused_rope=True))
+    assert st == skv.OK
+    assert skv.lib.rope_apply_window(h, ctypes.c_void_p(0)) == skv.ERR_STATE
+    skv.lib.kv_cache_destroy(h)
