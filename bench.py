@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--bc-chunks", type=int, default=None,
                     help="query chunks of the many-chunk block-causal leg after the prefill frames "
                          "(default: the workload's chunk count, at most 22)")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the block-causal and guidance legs (profiler runs: only the timed schedule)")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy the cache out once (plain row copies of known size) so that "
                          "counter passes can scale FETCH_SIZE / WRITE_SIZE")
@@ -418,7 +420,7 @@ def main():
     if wl.text_tokens:
         xf = 4.0 * lq * wl.text_tokens * d * h
         out["cross_attention"] = {"tflops": round(xf / (cross_ms * 1e-3) / 1e12, 2), "avg_ms": round(cross_ms, 4)}
-    if bf16 and wl.layers == 1:
+    if bf16 and wl.layers == 1 and not args.no_legs:
         out["block_causal"] = block_causal_leg(r, args)
         out["guidance_batch"] = guidance_leg(r)
     if not args.no_cpu_baseline and wl.layers == 1:
