@@ -425,6 +425,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   // unmasked: the running max starts at the first half tile's max; masked: at -inf (a row may
   // see no key of the first tiles) and follows every half tile's max
   float m_run = MASKED ? -INFINITY : 0.f, l_run = 0.f;
+  // unmasked: -m_run in every entry, the accumulator the score products start from, so the
+  // scores come out already relative to the running max (no subtraction per score)
+  f32x16_t negm;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
 
   // Masked (many chunks at once): query row r lies in frame q0 + r / F of the chunk ending at
   // frame e(r); it sees keys of frames j < e with j < S or j >= e - (W - S).  This workgroup's
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   };
   int kq_off[KI], vq_off[VI];  // byte offsets for whole tiles of the current range
 
-  // Two uniform tile iterators over the key ranges: K runs ahead of V.
+  // Two uniform tile iterators over the key ranges (one for K, one for V^T; they advance together).
   auto seg_n = [&](int s_) -> int { return MASKED ? (s_ == 0 ? sink_keys : ring_keys) : a.seg[s_].n; };
   auto seg_start = [&](int s_) -> int { return MASKED ? (s_ == 0 ? 0 : ring0) : 0; };
   int n_tiles = 0, alt_tiles = 1 << 30;  // tiles before the ranges that use the queries at q_alt
@@ -595,27 +600,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   const int voff = l32 * VP + 16 * hf;
   const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  // Two stages: K runs one half-tile ahead of V (K0, V0, K1 in flight at the start), two
-  // barriers per tile.  Four stages: whole tiles NSTAGE-2 ahead, one barrier per tile.
-  int nk_k[2] = {0, 0}, k0_k[2] = {0, 0};        // two stages: per stage
-  int nkq[3] = {0, 0, 0}, k0q[3] = {0, 0, 0};    // four stages: the next tiles, oldest first
-  if constexpr (NSTAGE == 2) {
-    nk_k[0] = issue_k(0);
-    k0_k[0] = key0;
-    issue_v(0);
-    if (n_tiles > 1) {
-      nk_k[1] = issue_k(1);
-      k0_k[1] = key0;
-    }
-  } else {
+  // Whole K/V tiles NSTAGE-1 ahead (two stages: one ahead), one barrier per tile.
+  int nkq[3] = {0, 0, 0}, k0q[3] = {0, 0, 0};  // valid keys / first key of the tiles in flight, oldest first
 #pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i)
-      if (i < n_tiles) {
-        nkq[i] = issue_k(i);
-        k0q[i] = key0;
-        issue_v(i);
-      }
-  }
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    if (i < n_tiles) {
+      nkq[i] = issue_k(i);
+      k0q[i] = key0;
+      issue_v(i);
+    }
 
   // P = exp2(S' - sub) for one 32-key half, packed to bf16 in B-operand order; returns the
   // row sum of the rounded values.
@@ -686,39 +679,28 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   };
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int st = NSTAGE == 2 ? (t & 1) : (t & 3);
+    const int st = t % NSTAGE;
     const bool more = t + 1 < n_tiles;
-    int nk, k0;
-    if constexpr (NSTAGE == 2) {
-      // K_t landed (V_t and K_{t+1} may still be in flight), then everyone's V_{t-1} reads are done.
-      if (more)
-        wait_vm_barrier<KMIN + VMIN>();
-      else
-        wait_vm_barrier<VMIN>();
-      if (more) issue_v(st ^ 1);
-      nk = nk_k[st];
-      k0 = k0_k[st];
-    } else {
-      // tile t landed (up to two later tiles may still be in flight), then everyone is done
-      // with tile t-1, whose stage takes tile t+3
-      if (t + 2 < n_tiles)
-        wait_vm_barrier<2 * (KMIN + VMIN)>();
-      else if (more)
-        wait_vm_barrier<KMIN + VMIN>();
-      else
-        wait_vm_barrier<0>();
-      nk = nkq[0];
-      k0 = k0q[0];
-      nkq[0] = nkq[1];
-      nkq[1] = nkq[2];
-      k0q[0] = k0q[1];
-      k0q[1] = k0q[2];
-      if (t + NSTAGE - 1 < n_tiles) {
-        const int sn = (t + NSTAGE - 1) & 3;
-        nkq[2] = issue_k(sn);
-        k0q[2] = key0;
-        issue_v(sn);
-      }
+    // tile t landed (later tiles may still be in flight), then everyone is done with tile t-1,
+    // whose stage takes tile t + NSTAGE - 1
+    if constexpr (NSTAGE == 2)
+      wait_vm_barrier<0>();
+    else if (t + 2 < n_tiles)
+      wait_vm_barrier<2 * (KMIN + VMIN)>();
+    else if (more)
+      wait_vm_barrier<KMIN + VMIN>();
+    else
+      wait_vm_barrier<0>();
+    const int nk = nkq[0], k0 = k0q[0];
+    nkq[0] = nkq[1];
+    nkq[1] = nkq[2];
+    k0q[0] = k0q[1];
+    k0q[1] = k0q[2];
+    if (t + NSTAGE - 1 < n_tiles) {
+      const int sn = (t + NSTAGE - 1) % NSTAGE;
+      nkq[NSTAGE - 2] = issue_k(sn);
+      k0q[NSTAGE - 2] = key0;
+      issue_v(sn);
     }
 
     if (t == alt_tiles) load_q(a.q_alt);
@@ -729,7 +711,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = ld_bf16x8(kt + koff[0] + 32 * ks);
     __builtin_amdgcn_sched_barrier(0);
-    f32x16_t s0 = {};
+    f32x16_t s0 = negm;
+    if constexpr (MASKED) s0 = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s0, 0, 0, 0);
     float sub0;
@@ -747,12 +730,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       if (t == 0) {
         // first tile: the running max starts at the max of its first half (key 0 is always valid)
         m_run = max_half(s0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] -= m_run;
+          negm[r] = -m_run;
+        }
       }
-      sub0 = m_run;
+      sub0 = 0.f;
     }
 
     // ---- keys 32..63 on the matrix cores while P of keys 0..31 is formed
-    f32x16_t s1 = {};
+    f32x16_t s1 = negm;
+    if constexpr (MASKED) s1 = f32x16_t{};
     bf16x8_t pb[4];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = ld_bf16x8(kt + koff[1] + 32 * ks);
@@ -768,8 +757,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     // The running max is raised only when some score exceeds it by a lot (a row sum past
     // 2^60): the result is the same for any max, and P stays far below overflow.
     if (!MASKED && __any(lsum > 0x1p60f)) {
-      raise_by(fmaxf(max_half(s0) - m_run, 0.f));
-      lsum = exp_half(s0, m_run, pb[0], pb[1]);
+      // scores are relative to the old max (s1 too, its product started from the old -m_run)
+      const float up = fmaxf(max_half(s0), 0.f);
+      raise_by(up);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] -= up;
+        s1[r] -= up;
+        negm[r] = -m_run;
+      }
+      lsum = exp_half(s0, 0.f, pb[0], pb[1]);
     }
     l_run += lsum;
     if constexpr (MASKED) {
@@ -780,18 +777,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (score_key(r, 0) >= nkh) s1[r] = -INFINITY;
-    }
-
-    if constexpr (NSTAGE == 2) {
-      // V_t landed (K_{t+1} and V_{t+1} may still be in flight), then everyone's K_t reads are done
-      if (more)
-        wait_vm_barrier<KMIN + VMIN>();
-      else
-        wait_vm_barrier<0>();
-      if (t + 2 < n_tiles) {
-        nk_k[st] = issue_k(st);
-        k0_k[st] = key0;
-      }
     }
 
     // ---- O^T += V^T P^T over keys 0..31 while P of keys 32..63 is formed
@@ -810,15 +795,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     if constexpr (MASKED) {
       lsum = exp_half(s1, follow_max(s1), pb[2], pb[3]);
     } else {
-      lsum = exp_half(s1, m_run, pb[2], pb[3]);
+      lsum = exp_half(s1, 0.f, pb[2], pb[3]);
 #pragma unroll
       for (int i = 0; i < 2 * MBLK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * MBLK), 0);
       }
       if (__any(lsum > 0x1p60f)) {
-        raise_by(fmaxf(max_half(s1) - m_run, 0.f));
-        lsum = exp_half(s1, m_run, pb[2], pb[3]);
+        const float up = fmaxf(max_half(s1), 0.f);
+        raise_by(up);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s1[r] -= up;
+          negm[r] = -m_run;
+        }
+        lsum = exp_half(s1, 0.f, pb[2], pb[3]);
       }
     }
     l_run += lsum;
