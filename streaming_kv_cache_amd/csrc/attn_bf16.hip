@@ -350,9 +350,11 @@ constexpr int kRsrcWord3 = 0x00020000;
 // A buffer load rather than a global one: the compiler then tracks it as a plain vector-memory
 // load, and LDS reads issued after it keep their partial lgkmcnt waits.  Offsets stay below 2^31
 // (the host checks the ranges).
-__device__ __forceinline__ void buf_lds16(const void* base, void* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kRsrcWord3),
-                                           lds_ptr(lds), 16, voff, soff, 0, 0);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kRsrcWord3);
+}
+__device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 16, voff, soff, 0, 0);
 }
 
 // Wait until at most N vector-memory loads of this wave are in flight and all LDS
@@ -483,11 +485,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   const uint8_t* kp = nullptr;
   
   int k_so = 0, kkey = 0;  // kkey: sequence index of the next K tile's first key (masked)
+  __amdgpu_buffer_rsrc_t krs = buf_rsrc(nullptr);  // the current K range of this head (k_so: offset in it)
   auto k_seg = [&](int s_) {
     const KvSeg sg = a.seg[MASKED ? 0 : s_];
     const int start = seg_start(s_);
     kp = (const uint8_t*)sg.k + 2 * ((int64_t)h * sg.k_hs + (int64_t)start * sg.k_rs);
     k_so = 0;
+    krs = buf_rsrc(kp);
     kkey = start;
     k_rs_b = (int)(2 * sg.k_rs);
     krem = seg_n(s_);
@@ -502,11 +506,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   const uint8_t* vp = nullptr;
   
   int v_so = 0;
+  __amdgpu_buffer_rsrc_t vrs = buf_rsrc(nullptr);
   auto v_seg = [&](int s_) {
     const KvSeg sg = a.seg[MASKED ? 0 : s_];
     const int start = seg_start(s_);
     vp = (const uint8_t*)sg.v + 2 * ((int64_t)h * sg.v_hs + (int64_t)start * sg.v_rs);
     v_so = 0;
+    vrs = buf_rsrc(vp);
     v_ds_b = (int)(2 * sg.v_ds);
     vrem = seg_n(s_);
     v_al16 = sg.v_al16 && (start & 7) == 0;
@@ -534,7 +540,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
         const int blk = wave + NW * i;
-        if (blk < KBLK) buf_lds16(kp - k_so, dst + blk * 1024, kq_off[i], k_so);
+        if (blk < KBLK) buf_lds16(krs, dst + blk * 1024, kq_off[i], k_so);
       }
     } else {
       int ln = lane;
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
           int row, c16;
           k_lane(i, ln, row, c16);
           const int rr = row < nk ? row : 0;  // rows past the range: a valid row (masked)
-          buf_lds16(kp - k_so, dst + blk * 1024, rr * k_rs_b + c16, k_so);
+          buf_lds16(krs, dst + blk * 1024, rr * k_rs_b + c16, k_so);
         }
       }
     }
@@ -564,7 +570,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 #pragma unroll
       for (int i = 0; i < VI; ++i) {
         const int blk = wave + NW * i;
-        if (blk < VBLK) buf_lds16(vp - v_so, dst + blk * 1024, vq_off[i], v_so);
+        if (blk < VBLK) buf_lds16(vrs, dst + blk * 1024, vq_off[i], v_so);
       }
     } else if (v_al16) {
       int ln = lane;
@@ -576,7 +582,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
           int d, ch;
           v_lane(i, ln, d, ch);
           const int cc = 8 * ch < nk ? ch : 0;  // chunks past the range: valid data, P is 0
-          buf_lds16(vp - v_so, dst + blk * 1024, d * v_ds_b + 16 * cc, v_so);
+          buf_lds16(vrs, dst + blk * 1024, d * v_ds_b + 16 * cc, v_so);
         }
       }
     } else {
