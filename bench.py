@@ -311,6 +311,44 @@ def guidance_leg(runner):
             "two_calls_tflops": round(flop / (t["single"] * 1e-3) / 1e12, 2)}
 
 
+def hbm_leg(runner, reps=10):
+    """The HBM-bound kernels launched back to back (reps launches between two events), which leaves
+    out most of the per-launch event and dispatch overhead the in-schedule timings carry."""
+    import torch
+    skv, cfg, wl = runner.skv, runner.cfg, runner.wl
+    cache = runner.caches[0]
+    q, k, v, noise = runner.pool[0][wl.passes - 1]
+    elt = 2 if cfg.dtype == skv.BF16 else 4
+    tensor = cfg.chunk_frames * cfg.tokens_per_frame * cfg.heads * cfg.head_dim * elt
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3   # us per launch
+
+    kk = k if runner.rel or runner.fused else runner.kr[0]
+    res = {}
+    us = timed(lambda: cache.append_evict(kk, v))
+    res["append"] = {"avg_us": round(us, 2), "GB/s": round(4 * tensor / us / 1e3, 1),
+                     "frac_hbm": round(4 * tensor / us / 1e3 / HBM_PEAK_GBS, 4)}
+    us = timed(lambda: cache.stage_v(v))
+    res["stage_v"] = {"avg_us": round(us, 2), "GB/s": round(2 * tensor / us / 1e3, 1)}
+    if not runner.fused:
+        t0 = cache.info().n_appended
+        us = timed(lambda: cache.rope_apply(q, out=runner.qr, start_frame=t0))
+        res["rope_one_tensor"] = {"avg_us": round(us, 2), "GB/s": round(2 * tensor / us / 1e3, 1)}
+    if wl.timesteps:
+        us = timed(lambda: skv.sampler_step(runner.x, runner.out, 0.75, 0.5, noise=noise, x0_out=runner.x0,
+                                            x_next_out=runner.x))
+        res["sampler_renoise"] = {"avg_us": round(us, 2), "GB/s": round(5 * tensor / us / 1e3, 1)}
+    return res
+
+
 def traffic_from_profile(wl_name, per_launch_algo_bytes):
     """HBM bytes per attention launch from committed rocprofv3 counters, if taken on the current kernel."""
     p = os.path.join(ROOT, "profiles", f"attn_bf16_{wl_name}_counters.json")
@@ -420,6 +458,8 @@ def main():
     if wl.text_tokens:
         xf = 4.0 * lq * wl.text_tokens * d * h
         out["cross_attention"] = {"tflops": round(xf / (cross_ms * 1e-3) / 1e12, 2), "avg_ms": round(cross_ms, 4)}
+    if wl.layers == 1 and not args.no_legs:
+        out["hbm_back_to_back"] = hbm_leg(r)
     if bf16 and wl.layers == 1 and not args.no_legs:
         out["block_causal"] = block_causal_leg(r, args)
         out["guidance_batch"] = guidance_leg(r)
