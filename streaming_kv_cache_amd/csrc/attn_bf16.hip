@@ -392,7 +392,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * (KT_B + VT_B)];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
+  // uniform (scalar branches on it) and known to be below NW
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
   const int l32 = lane & 31, hf = lane >> 5;
   // every batch element has the same Lq and H
   const int n_qt = (ab.b[0].Lq + BM - 1) / BM;
