@@ -333,6 +333,13 @@ def hbm_leg(runner, reps=10):
 
     kk = k if runner.rel or runner.fused else runner.kr[0]
     res = {}
+    # context: one plain device copy of the same byte count as the append (K and V in, K and V out)
+    src = torch.empty(2 * tensor, dtype=torch.uint8, device=k.device)
+    dst = torch.empty_like(src)
+    us = timed(lambda: dst.copy_(src))
+    res["plain_copy_same_bytes"] = {"avg_us": round(us, 2), "GB/s": round(4 * tensor / us / 1e3, 1),
+                                    "frac_hbm": round(4 * tensor / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del src, dst
     us = timed(lambda: cache.append_evict(kk, v))
     res["append"] = {"avg_us": round(us, 2), "GB/s": round(4 * tensor / us / 1e3, 1),
                      "frac_hbm": round(4 * tensor / us / 1e3 / HBM_PEAK_GBS, 4)}
