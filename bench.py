@@ -45,10 +45,32 @@ def parse():
                          "(default: the workload's chunk count, at most 22)")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the block-causal and guidance legs (profiler runs: only the timed schedule)")
+    ap.add_argument("--rollout", action="store_true",
+                    help="run the workload's whole rollout through the full schedule instead of warm-up + steps: "
+                         "the steady chunks are timed, and per-chunk time and device memory of the first 50 steady "
+                         "chunks are compared with the last 50 (the bounded cache keeps both constant)")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy the cache out once (plain row copies of known size) so that "
                          "counter passes can scale FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
+
+
+def box_peak(torch):
+    """Dense bf16 peak from what the box reports: CUs x 4096 flop per clock x the peak engine clock
+    (hipDeviceAttributeClockRate, kHz).  None where the runtime does not answer."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        # hipDeviceGetAttribute(int*, hipDeviceAttribute_t, int); hipDeviceAttributeClockRate is 5 in
+        # hip_runtime_api.h (EccEnabled 0, AccessPolicyMaxWindowSize, AsyncEngineCount,
+        # CanMapHostMemory, CanUseHostPointerForRegisteredMem, ClockRate)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, torch.cuda.current_device()) != 0 or khz.value <= 0:
+            return None
+    except OSError:
+        return None
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    return {"cus": cus, "sclk_mhz": khz.value / 1e3, "tflops": round(cus * 4096 * khz.value * 1e3 / 1e12, 1)}
 
 
 def kernel_sha(name: str) -> str:
@@ -87,6 +109,8 @@ class Runner:
         if wl.text_tokens:
             tshape = (wl.text_tokens, h, d)
             self.text = [si.draw(tshape, 0, 0, 0, si.TEXT_K, dt).cuda(), si.draw(tshape, 0, 0, 0, si.TEXT_V, dt).cuda()]
+            # the prompt's K/V are laid out once and attended by every chunk and pass
+            self.text_cache = skv.TextCache(self.text[0], self.text[1])
             self.xout = torch.empty(shape, dtype=dt, device="cuda")
         self.qr = torch.empty(shape, dtype=dt, device="cuda")
         self.kr = [torch.empty(shape, dtype=dt, device="cuda") for _ in range(wl.layers)]
@@ -148,7 +172,7 @@ class Runner:
                     self._ev("attn1")
                 if wl.text_tokens:
                     self._ev("cross0")
-                    self.skv.cross_attention(q, self.text[0], self.text[1], out=self.xout)
+                    self.text_cache.attend(q, out=self.xout)
                     self._ev("cross1")
                 if p == wl.passes - 1:
                     self._ev("app0")
@@ -384,19 +408,34 @@ def main():
     torch.cuda.set_device(0)
     r = Runner(wl, max(1, args.pool))
     r.prefill()
-    while r.visible() < cfg.window_frames:   # fill the window (not timed, no attention launches)
-        r.fill_step()
-    for _ in range(args.warmup):
-        r.step()
+    mem = None
+    if args.rollout:
+        # the whole rollout from its first chunk: chunks before the window fills run untimed
+        while r.visible() < cfg.window_frames:
+            r.step()
+        args.warmup, args.steps = r.chunk, wl.n_chunks - r.chunk
+    else:
+        while r.visible() < cfg.window_frames:   # fill the window (not timed, no attention launches)
+            r.fill_step()
+        for _ in range(args.warmup):
+            r.step()
     torch.cuda.synchronize()
     r.ev = {k: [] for k in ("step0", "step1", "win0", "win1", "rope0", "rope1", "stage0", "attn0", "attn1",
                             "cross0", "cross1", "app0", "app1", "samp0", "samp1")}
     torch.cuda.synchronize()
+    if args.rollout:
+        torch.cuda.reset_peak_memory_stats()
+        mem = {"allocated_first_steady_MB": round(torch.cuda.memory_allocated() / 2**20, 1)}
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         r.step()
+        if args.rollout and (i + 1) % 25 == 0:
+            print(f"[rollout] chunk {r.chunk} of {wl.n_chunks} enqueued", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if mem is not None:
+        mem["allocated_last_MB"] = round(torch.cuda.memory_allocated() / 2**20, 1)
+        mem["max_allocated_MB"] = round(torch.cuda.max_memory_allocated() / 2**20, 1)
     ev = r.ev
     ms_step = wall * 1e3 / args.steps
     if args.calibrate:
@@ -425,6 +464,8 @@ def main():
             "frac": round(attn_tflops / peak, 4),
             "traffic": traffic_from_profile(wl.name, None), "kernel": "attn_bf16_vt_kernel" if bf16 else "attn_f32_kernel",
             "avg_kernel_ms": round(attn_ms, 4), "algorithmic_flop_per_launch": attn_flop}
+    if bf16:
+        roof["box_formula_peak"] = box_peak(torch)
     out = {
         "metric": "chunk-attention TFLOP/s + % bf16 MFMA peak; cache-update GB/s; per-chunk ms",
         "value": round(step_flop / (ms_step * 1e-3) / 1e12, 2),
@@ -464,7 +505,24 @@ def main():
         out["rope_window"] = {"GB/s": round(win_bytes / (win_ms * 1e-3) / 1e9, 1), "avg_us": round(win_ms * 1e3, 2)}
     if wl.text_tokens:
         xf = 4.0 * lq * wl.text_tokens * d * h
-        out["cross_attention"] = {"tflops": round(xf / (cross_ms * 1e-3) / 1e12, 2), "avg_ms": round(cross_ms, 4)}
+        out["cross_attention"] = {"tflops": round(xf / (cross_ms * 1e-3) / 1e12, 2), "avg_ms": round(cross_ms, 4),
+                                  "path": "text_cache_prepare once + cross_attention_cached"}
+        # context: the same product through cross_attention (token-major text V, no preparation)
+        q0 = r.pool[0][0][0]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        skv.cross_attention(q0, r.text[0], r.text[1], out=r.xout)
+        e0.record()
+        for _ in range(10):
+            skv.cross_attention(q0, r.text[0], r.text[1], out=r.xout)
+        e1.record()
+        torch.cuda.synchronize()
+        out["cross_attention"]["unprepared_tflops"] = round(xf / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12, 2)
+    if mem is not None:
+        n50 = min(50, len(steps_ms) // 2)
+        first, last = float(np.mean(steps_ms[:n50])), float(np.mean(steps_ms[-n50:]))
+        out["constancy"] = {"chunks": wl.n_chunks, "steady_from_chunk": args.warmup, "window": n50,
+                            "first_steady_ms": round(first, 3), "last_ms": round(last, 3),
+                            "last_over_first": round(last / first, 4), "memory": mem}
     if wl.layers == 1 and not args.no_legs:
         out["hbm_back_to_back"] = hbm_leg(r)
     if bf16 and wl.layers == 1 and not args.no_legs:

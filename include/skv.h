@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 2
+#define SKV_ABI_VERSION 3
 
 typedef enum {
   SKV_OK = 0,
@@ -190,6 +190,29 @@ skv_status chunk_attention_batch(const skv_cache* const* caches, int32_t n_cache
 skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const void* v_text,
                            int32_t n_text, int32_t heads, int32_t head_dim, int32_t dtype, void* out,
                            void* stream);
+
+/* Prepared text cache for cross attention.  The text K/V are computed once per
+ * prompt and reused by every later chunk and pass ([LB-fast] "3. KV 缓存 滚动窗口",
+ * its note on the cross-attention cache; [ABot-stream] "一次流式生成的完整链路",
+ * step 1: the 512-token text cache is built once, and a prompt change rebuilds
+ * only it), so their layout is fixed once:
+ * text_cache_prepare copies k_text and stores v_text transposed (V^T rows of the
+ * keys, padded to a multiple of 64 with zeros) into `store`, a caller-allocated
+ * device buffer of text_cache_bytes(...) bytes, 256-byte aligned.  bf16: the
+ * copy of k_text [n_text, H, D] is followed, at the next 256-byte boundary, by
+ * V^T [H][D][roundup(n_text, 64)]; fp32: copies of k_text and v_text back to back.
+ * cross_attention_cached then attends q/out [n_q, H, D] over the store with the
+ * same result definition as cross_attention (bf16: the matrix-core kernel of
+ * chunk_attention, which reads V^T with direct-to-LDS loads).  The store is
+ * read-only for cross_attention_cached; replacing the prompt means preparing
+ * again.  Same checks as cross_attention (heads 1..4096; bf16 D 64/128, fp32 D
+ * 32/64/128; 1 <= n_text <= 2^30); SKV_ERR_SHAPE also when a head's keys do not
+ * fit the bf16 kernel's 32-bit offsets. */
+skv_status text_cache_bytes(int32_t n_text, int32_t heads, int32_t head_dim, int32_t dtype, size_t* bytes);
+skv_status text_cache_prepare(const void* k_text, const void* v_text, int32_t n_text, int32_t heads,
+                              int32_t head_dim, int32_t dtype, void* store, void* stream);
+skv_status cross_attention_cached(const void* q, int32_t n_q, const void* store, int32_t n_text,
+                                  int32_t heads, int32_t head_dim, int32_t dtype, void* out, void* stream);
 
 /* Host-side bookkeeping of the handle. */
 skv_status kv_cache_info(const skv_cache* cache, kv_cache_info_t* info);

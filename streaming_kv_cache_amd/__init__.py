@@ -26,6 +26,7 @@ EXPORTED = (
     "kv_cache_destroy", "kv_cache_append_evict", "rope_apply", "rope_apply_window", "chunk_attention",
     "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v", "sampler_step",
     "chunk_attention_batch", "block_causal_workspace_bytes", "block_causal_attention",
+    "text_cache_bytes", "text_cache_prepare", "cross_attention_cached",
 )
 
 
@@ -81,6 +82,9 @@ def _load() -> ctypes.CDLL:
         "block_causal_attention": ([ctypes.POINTER(SkvConfig), vp, vp, vp, i32, i32, vp, vp, vp], st),
         "sampler_step": ([vp, vp, vp, ctypes.c_double, vp, i64, ctypes.c_double, ctypes.c_double, i32, vp, vp, vp],
                          st),
+        "text_cache_bytes": ([i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)], st),
+        "text_cache_prepare": ([vp, vp, i32, i32, i32, i32, vp, vp], st),
+        "cross_attention_cached": ([vp, i32, vp, i32, i32, i32, i32, vp, vp], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -309,6 +313,55 @@ def cross_attention(q: torch.Tensor, k_text: torch.Tensor, v_text: torch.Tensor,
     _check(lib.cross_attention(_ptr(q), q.shape[0], _ptr(k_text), _ptr(v_text), k_text.shape[0], q.shape[1],
                                q.shape[2], _dtype_code(q.dtype), _ptr(out), _stream(stream)), "cross_attention")
     return out
+
+
+def text_cache_bytes(n_text: int, heads: int, head_dim: int, dtype: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib.text_cache_bytes(int(n_text), int(heads), int(head_dim), int(dtype), ctypes.byref(b)),
+           "text_cache_bytes")
+    return b.value
+
+
+def text_cache_prepare(k_text: torch.Tensor, v_text: torch.Tensor, store: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Lay the text K/V out once for cross_attention_cached (see skv.h); returns the store (uint8)."""
+    if k_text.dim() != 3 or k_text.shape != v_text.shape:
+        raise ValueError("k_text/v_text [n_text, H, D] expected")
+    for t in (k_text, v_text):
+        if t.dtype != k_text.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("contiguous CUDA tensors of one dtype expected")
+    n, h, d = k_text.shape
+    dt = _dtype_code(k_text.dtype)
+    if store is None:
+        store = torch.empty(text_cache_bytes(n, h, d, dt), dtype=torch.uint8, device=k_text.device)
+    _check(lib.text_cache_prepare(_ptr(k_text), _ptr(v_text), n, h, d, dt, _ptr(store), _stream(stream)),
+           "text_cache_prepare")
+    return store
+
+
+def cross_attention_cached(q: torch.Tensor, store: torch.Tensor, n_text: int, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """cross_attention over a store laid out by text_cache_prepare; q [n_q, H, D] on the GPU."""
+    if q.dim() != 3 or not q.is_cuda or not q.is_contiguous() or not store.is_cuda:
+        raise ValueError("contiguous CUDA q [n_q, H, D] and a CUDA store expected")
+    out = torch.empty_like(q) if out is None else out
+    _check(lib.cross_attention_cached(_ptr(q), q.shape[0], _ptr(store), int(n_text), q.shape[1], q.shape[2],
+                                      _dtype_code(q.dtype), _ptr(out), _stream(stream)), "cross_attention_cached")
+    return out
+
+
+class TextCache:
+    """Text K/V of one prompt, laid out once (text_cache_prepare) and attended by every chunk and pass."""
+
+    def __init__(self, k_text: torch.Tensor, v_text: torch.Tensor, stream=None):
+        self.n_text, self.heads, self.head_dim = k_text.shape
+        self.dtype = k_text.dtype
+        self.store = text_cache_prepare(k_text, v_text, stream=stream)
+
+    def attend(self, q: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        if q.dtype != self.dtype or tuple(q.shape[1:]) != (self.heads, self.head_dim):
+            raise ValueError(f"q: expected [n_q, {self.heads}, {self.head_dim}] of {self.dtype}")
+        return cross_attention_cached(q, self.store, self.n_text, out=out, stream=stream)
 
 
 def sampler_step(x_t: torch.Tensor, v_cond: torch.Tensor, sigma: float, sigma_next: float = 0.0,

@@ -473,6 +473,111 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
   return e == hipSuccess ? SKV_OK : SKV_ERR_HIP;
 }
 
+// Prepared text cache: [copy of k_text, n_text*H*D] [256-byte boundary] [bf16: V^T, H*D*pad | fp32: v_text copy].
+struct TextLayout {
+  int64_t k_bytes = 0, vt_off = 0, total = 0, pad = 0;
+};
+
+static skv_status text_layout(int32_t n_text, int32_t heads, int32_t head_dim, int32_t dtype, TextLayout* L) {
+  if (heads < 1 || heads > 4096) return SKV_ERR_CONFIG;
+  if (!skv::attention_head_dim_supported(dtype, head_dim)) return SKV_ERR_CONFIG;
+  if (n_text < 1 || n_text > (1 << 30)) return SKV_ERR_SHAPE;
+  const int64_t elt = dtype == SKV_BF16 ? 2 : 4;
+  L->k_bytes = (int64_t)n_text * heads * head_dim * elt;
+  L->pad = ((int64_t)n_text + 63) / 64 * 64;
+  L->vt_off = (L->k_bytes + 255) / 256 * 256;
+  if (dtype == SKV_BF16) {
+    // the matrix-core kernel addresses one head's keys with 32-bit byte offsets: token-major K rows
+    // (H*D apart, plus one tile of slack) and V^T rows of pad keys
+    if (((int64_t)n_text + 64) * heads * head_dim * 2 > INT32_MAX || (int64_t)head_dim * L->pad * 2 > INT32_MAX)
+      return SKV_ERR_SHAPE;
+    L->total = L->vt_off + (int64_t)heads * head_dim * L->pad * 2;
+  } else {
+    L->total = L->vt_off + L->k_bytes;
+  }
+  return SKV_OK;
+}
+
+static skv_status check_store(const void* store) {
+  if (!store) return SKV_ERR_NULL;
+  return ((uintptr_t)store & 255) ? SKV_ERR_ALIGN : SKV_OK;
+}
+
+skv_status text_cache_bytes(int32_t n_text, int32_t heads, int32_t head_dim, int32_t dtype, size_t* bytes) {
+  if (!bytes) return SKV_ERR_NULL;
+  TextLayout L;
+  const skv_status st = text_layout(n_text, heads, head_dim, dtype, &L);
+  if (st != SKV_OK) return st;
+  *bytes = (size_t)L.total;
+  return SKV_OK;
+}
+
+skv_status text_cache_prepare(const void* k_text, const void* v_text, int32_t n_text, int32_t heads,
+                              int32_t head_dim, int32_t dtype, void* store, void* stream) {
+  skv_status st;
+  if ((st = check_ptr(k_text)) != SKV_OK) return st;
+  if ((st = check_ptr(v_text)) != SKV_OK) return st;
+  if ((st = check_store(store)) != SKV_OK) return st;
+  TextLayout L;
+  if ((st = text_layout(n_text, heads, head_dim, dtype, &L)) != SKV_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(store, k_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s) != hipSuccess) return SKV_ERR_HIP;
+  char* vdst = (char*)store + L.vt_off;
+  if (dtype != SKV_BF16)
+    return hipMemcpyAsync(vdst, v_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s) == hipSuccess ? SKV_OK
+                                                                                                 : SKV_ERR_HIP;
+  // values -> V^T rows [h][d][key], keys past n_text zero up to the padded row length
+  skv::WriteArgs wa{};
+  wa.k_src = nullptr;
+  wa.v_src = v_text;
+  wa.tok_stride = (int64_t)heads * head_dim;
+  wa.head_stride = head_dim;
+  wa.vt_dst = vdst;
+  wa.vt_hs = (int64_t)head_dim * L.pad;
+  wa.vt_ds = L.pad;
+  wa.nruns = 0;
+  wa.F = n_text;
+  wa.H = heads;
+  wa.D = head_dim;
+  wa.n_tok = n_text;
+  wa.row_pad = (int32_t)L.pad;
+  return skv::launch_write_kv(wa, 2, s) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+}
+
+skv_status cross_attention_cached(const void* q, int32_t n_q, const void* store, int32_t n_text, int32_t heads,
+                                  int32_t head_dim, int32_t dtype, void* out, void* stream) {
+  skv_status st;
+  if ((st = check_ptr(q)) != SKV_OK) return st;
+  if ((st = check_ptr(out)) != SKV_OK) return st;
+  if ((st = check_store(store)) != SKV_OK) return st;
+  TextLayout L;
+  if ((st = text_layout(n_text, heads, head_dim, dtype, &L)) != SKV_OK) return st;
+  if (n_q < 1 || (int64_t)n_q * heads > (int64_t)INT32_MAX / 2) return SKV_ERR_SHAPE;
+  if (dtype == SKV_BF16 && ((int64_t)n_q + 64) * heads * head_dim * 2 > INT32_MAX) return SKV_ERR_SHAPE;
+  const char* vsrc = (const char*)store + L.vt_off;
+  const hipStream_t s = (hipStream_t)stream;
+  skv::AttnBatch ab{};
+  ab.nb = 1;
+  skv::AttnArgs& a = ab.b[0];
+  a.q = q;
+  a.out = out;
+  a.alt_seg = 1 << 20;
+  a.Lq = n_q;
+  a.H = heads;
+  a.sl2 = softmax_scale_log2(head_dim);
+  a.nseg = 1;
+  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  if (dtype == SKV_BF16) {
+    // K token-major as given; V^T rows of L.pad keys per (head, dim)
+    a.seg[0] = skv::KvSeg{store, vsrc, (int64_t)head_dim, (int64_t)heads * head_dim, (int64_t)head_dim * L.pad, 1,
+                          L.pad, n_text, 1};
+    return skv::launch_attention_bf16_vt(ab, head_dim, s) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+  }
+  a.seg[0] = skv::KvSeg{store, vsrc, (int64_t)head_dim, (int64_t)heads * head_dim, (int64_t)head_dim,
+                        (int64_t)heads * head_dim, 1, n_text, 0};
+  return skv::launch_attention_f32(a, head_dim, s) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+}
+
 // Many-chunk attention: checks shared by the size query and the call.
 static skv_status block_causal_geometry(const skv_config* cfg, int32_t n_frames, int32_t q_frame0,
                                         skv::Geometry* g, int64_t* row_pad) {

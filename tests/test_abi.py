@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert skv.lib.skv_abi_version() == 2
+    assert skv.lib.skv_abi_version() == 3
     for code in range(7):
         assert skv.status_string(code)
     assert skv.status_string(99) == "unknown status"
@@ -116,6 +116,36 @@ def test_cross_attention_validation():
     assert f(p, 8, p, p, 0, 40, 128, skv.BF16, p, nul) == skv.ERR_SHAPE
     assert f(p, 0, p, p, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_SHAPE
     assert f(p, 8, p, p, 512, 0, 128, skv.BF16, p, nul) == skv.ERR_CONFIG
+
+
+def test_text_cache_sizes_and_validation():
+    """Store size formula, and every error path of the prepared text cache returns before anything is
+    enqueued (no GPU needed)."""
+    # bf16: K copy (512 x 40 x 128 x 2) then V^T rows padded to 64 keys, at a 256-byte boundary
+    assert skv.text_cache_bytes(512, 40, 128, skv.BF16) == 2 * 512 * 40 * 128 * 2
+    assert skv.text_cache_bytes(77, 3, 64, skv.BF16) == (77 * 3 * 64 * 2 + 255) // 256 * 256 + 3 * 64 * 128 * 2
+    assert skv.text_cache_bytes(77, 3, 64, skv.F32) == (77 * 3 * 64 * 4 + 255) // 256 * 256 + 77 * 3 * 64 * 4
+    b = ctypes.c_size_t()
+    f = skv.lib.text_cache_bytes
+    assert f(512, 40, 128, skv.BF16, None) == skv.ERR_NULL
+    assert f(512, 40, 96, skv.BF16, ctypes.byref(b)) == skv.ERR_CONFIG       # bf16 D in {64, 128}
+    assert f(512, 40, 32, skv.F32, ctypes.byref(b)) == skv.OK
+    assert f(0, 40, 128, skv.BF16, ctypes.byref(b)) == skv.ERR_SHAPE
+    assert f(512, 0, 128, skv.BF16, ctypes.byref(b)) == skv.ERR_CONFIG
+    assert f(1 << 22, 40, 128, skv.BF16, ctypes.byref(b)) == skv.ERR_SHAPE   # past 32-bit offsets per head
+    p, p16, nul = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x40010), ctypes.c_void_p(0)
+    g = skv.lib.text_cache_prepare
+    assert g(nul, p, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_NULL
+    assert g(p, p, 512, 40, 128, skv.BF16, nul, nul) == skv.ERR_NULL
+    assert g(p, p, 512, 40, 128, skv.BF16, p16, nul) == skv.ERR_ALIGN        # store: 256-byte aligned
+    assert g(p, p16, 512, 40, 96, skv.BF16, p, nul) == skv.ERR_CONFIG
+    assert g(p, p, 0, 40, 128, skv.BF16, p, nul) == skv.ERR_SHAPE
+    h = skv.lib.cross_attention_cached
+    assert h(nul, 8, p, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_NULL
+    assert h(p, 8, nul, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_NULL
+    assert h(p, 8, p16, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_ALIGN
+    assert h(p, 0, p, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_SHAPE
+    assert h(p, 8, p, 512, 40, 128, 7, p, nul) == skv.ERR_CONFIG
 
 
 def test_sampler_step_validation():

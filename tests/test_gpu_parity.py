@@ -237,6 +237,55 @@ def test_cross_attention(dtype, n_q, n_text, h, d):
     ro.assert_close(out, ref, dtype, "cross")
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("dtype,n_q,n_text,h,d", [
+    (skv.BF16, 1000, 512, 5, 128), (skv.BF16, 130, 77, 3, 64), (skv.BF16, 6240, 512, 40, 128),
+    (skv.F32, 70, 512, 2, 128), (skv.F32, 33, 9, 1, 32),
+])
+def test_cross_attention_cached(dtype, n_q, n_text, h, d, waves, monkeypatch):
+    """Prepared text cache (copy of K, V^T rows) + the matrix-core kernel against the oracle's
+    cross attention; both kernel shapes; the largest case is the 480P chunk against 512 text tokens."""
+    if dtype == skv.F32 and waves == "8":
+        pytest.skip("one fp32 kernel shape")
+    monkeypatch.setenv("SKV_ATTN_WAVES", waves)
+    say(f"[cross cached] dtype={dtype} n_q={n_q} n_text={n_text} h={h} d={d} waves={waves}")
+    tdt = torch.bfloat16 if dtype == skv.BF16 else torch.float32
+    q = si.draw((n_q, h, d), 0, 0, 0, si.Q, tdt)
+    kt = si.draw((n_text, h, d), 0, 0, 0, si.TEXT_K, tdt)
+    vt = si.draw((n_text, h, d), 0, 0, 0, si.TEXT_V, tdt)
+    tc = skv.TextCache(kt.cuda(), vt.cuda())
+    out = tc.attend(q.cuda())
+    again = tc.attend(q.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    rows = _rows(n_q) if n_q > 2000 else np.arange(n_q)
+    ref = so.cross_attention(ro.f64(q[torch.as_tensor(rows)]), ro.f64(kt), ro.f64(vt))
+    ro.assert_close(out[torch.as_tensor(rows, device=out.device)], ref, dtype, "cross cached")
+
+
+@pytest.mark.parametrize("dtype,n_text,h,d", [(skv.BF16, 77, 3, 64), (skv.BF16, 512, 4, 128), (skv.F32, 9, 2, 32)])
+def test_text_cache_layout(dtype, n_text, h, d):
+    """The prepared store holds the bytes the header states: the K copy, then (bf16) V^T rows of
+    roundup(n_text, 64) keys with zero padding, (fp32) the V copy, at the next 256-byte boundary."""
+    say(f"[text store] dtype={dtype} n_text={n_text} h={h} d={d}")
+    tdt = torch.bfloat16 if dtype == skv.BF16 else torch.float32
+    kt = si.draw((n_text, h, d), 0, 0, 1, si.TEXT_K, tdt).cuda()
+    vt = si.draw((n_text, h, d), 0, 0, 1, si.TEXT_V, tdt).cuda()
+    store = skv.text_cache_prepare(kt, vt)
+    torch.cuda.synchronize()
+    kb = kt.numel() * kt.element_size()
+    off = (kb + 255) // 256 * 256
+    assert store.numel() == skv.text_cache_bytes(n_text, h, d, dtype)
+    assert torch.equal(store[:kb].view(tdt).view(n_text, h, d), kt)
+    if dtype == skv.BF16:
+        pad = (n_text + 63) // 64 * 64
+        v_t = store[off:].view(tdt).view(h, d, pad)
+        assert torch.equal(v_t[:, :, :n_text], vt.permute(1, 2, 0))
+        assert not v_t[:, :, n_text:].any()
+    else:
+        assert torch.equal(store[off:off + kb].view(tdt).view(n_text, h, d), vt)
+
+
 def test_determinism():
     say("[determinism] small_rel twice")
     wl = WORKLOADS["small_rel"]
