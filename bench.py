@@ -162,8 +162,7 @@ class Runner:
                     self._ev("attn1")
                 else:
                     self._ev("rope0")
-                    cache.rope_apply(q, out=self.qr, start_frame=t)
-                    cache.rope_apply(k, out=self.kr[li], start_frame=t)
+                    cache.rope_apply_qk(q, k, q_out=self.qr, k_out=self.kr[li], start_frame=t)
                     self._ev("rope1")
                     self._ev("stage0")
                     cache.stage_v(v)

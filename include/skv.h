@@ -141,6 +141,14 @@ skv_status kv_cache_append_evict(skv_cache* cache, const void* k, const void* v,
 skv_status rope_apply(const skv_cache* cache, const void* x_in, void* x_out, int32_t n_frames,
                       int64_t start_frame, void* stream);
 
+/* q and k_cur of one chunk share their time ids ([LB-src] 改造③ rotates both with the
+ * same start_frame; [ABot-stream] 机制三 places both in the chunk's slots), so one
+ * launch rotates both: the same result as rope_apply(q_in -> q_out) followed by
+ * rope_apply(k_in -> k_out) with these n_frames / start_frame.  Each output may
+ * alias its own input; the q and k tensors must not overlap each other. */
+skv_status rope_apply_qk(const skv_cache* cache, const void* q_in, void* q_out, const void* k_in, void* k_out,
+                         int32_t n_frames, int64_t start_frame, void* stream);
+
 /* REL only: rotate the visible history k_raw (sinks, then the visible ring
  * frames oldest first) at time ids 0..n_vis-c-1 into the workspace, once per
  * chunk; its result serves every pass until the next append or reset. */

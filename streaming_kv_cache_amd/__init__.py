@@ -26,7 +26,7 @@ EXPORTED = (
     "kv_cache_destroy", "kv_cache_append_evict", "rope_apply", "rope_apply_window", "chunk_attention",
     "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v", "sampler_step",
     "chunk_attention_batch", "block_causal_workspace_bytes", "block_causal_attention",
-    "text_cache_bytes", "text_cache_prepare", "cross_attention_cached",
+    "text_cache_bytes", "text_cache_prepare", "cross_attention_cached", "rope_apply_qk",
 )
 
 
@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "kv_cache_destroy": ([vp], st),
         "kv_cache_append_evict": ([vp, vp, vp, i32, vp], st),
         "rope_apply": ([vp, vp, vp, i32, i64, vp], st),
+        "rope_apply_qk": ([vp, vp, vp, vp, vp, i32, i64, vp], st),
         "rope_apply_window": ([vp, vp], st),
         "chunk_attention": ([vp, vp, vp, vp, i32, vp, vp], st),
         "cross_attention": ([vp, i32, vp, vp, i32, i32, i32, i32, vp, vp], st),
@@ -216,6 +217,18 @@ class KVCache:
         out = torch.empty_like(x) if out is None else self._tensor(out, n, "out")
         _check(lib.rope_apply(self._h, _ptr(x), _ptr(out), n, int(start_frame), _stream(stream)), "rope_apply")
         return out
+
+    def rope_apply_qk(self, q: torch.Tensor, k: torch.Tensor, q_out: Optional[torch.Tensor] = None,
+                      k_out: Optional[torch.Tensor] = None, start_frame: int = 0, stream=None):
+        """q and k of one chunk rotated at the same time ids in one launch; returns (q_out, k_out)."""
+        n = q.shape[0] // self.cfg.tokens_per_frame
+        self._tensor(q, n, "q")
+        self._tensor(k, n, "k")
+        q_out = torch.empty_like(q) if q_out is None else self._tensor(q_out, n, "q_out")
+        k_out = torch.empty_like(k) if k_out is None else self._tensor(k_out, n, "k_out")
+        _check(lib.rope_apply_qk(self._h, _ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out), n, int(start_frame),
+                                 _stream(stream)), "rope_apply_qk")
+        return q_out, k_out
 
     def rope_apply_window(self, stream=None) -> None:
         _check(lib.rope_apply_window(self._h, _stream(stream)), "rope_apply_window")

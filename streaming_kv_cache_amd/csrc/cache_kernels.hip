@@ -92,12 +92,10 @@ constexpr int kRopeThreads = 256;
 constexpr int kRopeHeads = 8;
 
 struct RopeArgs {
-  TokView src, dst;
+  RopeJob jobs[3];     // per grid z: tensors, time id of launch frame 0 (before clamping), clamp (>= 0)
   FrameRun runs[3];
   int32_t nruns;
   int32_t F, gw, H, D;
-  int64_t t0;          // time id of launch frame 0 (before clamping)
-  int32_t clamp_max;   // >= 0: clamp time ids to [0, clamp_max]
   int32_t pair_h, pair_w;  // first pair index of the height / width parts
   int32_t n_tok;
   double omega[64];    // per pair, theta^(-2k/d_axis) with k counted inside its axis
@@ -159,14 +157,15 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeArgs a) {
       df = run.dst0 + (fi - run.start);
     }
   }
-  const T* s = (const T*)a.src.base + (int64_t)(sf * a.F + tok) * a.src.tok_stride + g * 8 + h0 * a.src.head_stride;
-  T* d = (T*)a.dst.base + (int64_t)(df * a.F + tok) * a.dst.tok_stride + g * 8 + h0 * a.dst.head_stride;
+  const RopeJob& j = a.jobs[blockIdx.z];
+  const T* s = (const T*)j.src.base + (int64_t)(sf * a.F + tok) * j.src.tok_stride + g * 8 + h0 * j.src.head_stride;
+  T* d = (T*)j.dst.base + (int64_t)(df * a.F + tok) * j.dst.tok_stride + g * 8 + h0 * j.dst.head_stride;
   typename IO::V x[kRopeHeads];
 #pragma unroll
   for (int i = 0; i < kRopeHeads; ++i)
-    if (i < nh) x[i] = IO::load(s + i * a.src.head_stride);
-  int64_t t = a.t0 + fi;
-  if (a.clamp_max >= 0) t = t < 0 ? 0 : (t > a.clamp_max ? a.clamp_max : t);
+    if (i < nh) x[i] = IO::load(s + i * j.src.head_stride);
+  int64_t t = j.t0 + fi;
+  if (j.clamp_max >= 0) t = t < 0 ? 0 : (t > j.clamp_max ? j.clamp_max : t);
   const int row = tok / a.gw, col = tok - row * a.gw;
   float cs[4], sn[4];
   const double two_pi = 6.283185307179586476925287;
@@ -180,21 +179,19 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < kRopeHeads; ++i)
-    if (i < nh) IO::rot_store(d + i * a.dst.head_stride, x[i], cs, sn);
+    if (i < nh) IO::rot_store(d + i * j.dst.head_stride, x[i], cs, sn);
 }
 
 hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream) {
+  if (L.njobs < 1 || L.njobs > 3) return hipErrorInvalidValue;
   RopeArgs a;
-  a.src = L.src;
-  a.dst = L.dst;
+  for (int i = 0; i < 3; ++i) a.jobs[i] = L.job[i < L.njobs ? i : 0];
   for (int i = 0; i < 3; ++i) a.runs[i] = i < L.nruns ? L.runs[i] : FrameRun{0, 0, 0, 0};
   a.nruns = L.nruns;
   a.F = L.F;
   a.gw = L.gw;
   a.H = L.H;
   a.D = L.D;
-  a.t0 = L.t0;
-  a.clamp_max = L.clamp_max;
   a.pair_h = L.rope_t / 2;
   a.pair_w = (L.rope_t + L.rope_h) / 2;
   a.n_tok = L.n_frames * L.F;
@@ -206,7 +203,7 @@ hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream) {
   for (; p < 64; ++p) a.omega[p] = 0.0;
   const int G = L.D / 8;
   const int tpb = kRopeThreads / G;
-  dim3 grid((a.n_tok + tpb - 1) / tpb, (L.H + kRopeHeads - 1) / kRopeHeads);
+  dim3 grid((a.n_tok + tpb - 1) / tpb, (L.H + kRopeHeads - 1) / kRopeHeads, L.njobs);
   if (L.dtype_bf16)
     hipLaunchKernelGGL(rope_kernel<__bf16>, grid, dim3(kRopeThreads), 0, stream, a);
   else

@@ -46,15 +46,21 @@ struct SamplerArgs {
 hipError_t launch_sampler(const SamplerArgs& a, int elt, hipStream_t stream);
 hipError_t launch_vt_to_tok(const WriteArgs& a, int elt, hipStream_t stream);
 
-struct RopeLaunch {
+// One tensor of a rotary launch: src -> dst at time ids t0 + frame (clamped to [0, clamp_max] if >= 0).
+struct RopeJob {
   TokView src, dst;
+  int64_t t0;
+  int32_t clamp_max;
+};
+// Up to three tensors with the same frames, grid and split share one launch (grid z = job).
+struct RopeLaunch {
+  RopeJob job[3];
+  int njobs;
   FrameRun runs[3];
   int nruns;
   int n_frames, F, gw, H, D;
   int rope_t, rope_h, rope_w;
   double theta;
-  int64_t t0;
-  int clamp_max;
   bool dtype_bf16;
 };
 hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream);

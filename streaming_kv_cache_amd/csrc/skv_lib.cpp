@@ -100,8 +100,9 @@ skv_status stage_v(skv_cache* c, const void* v_cur, void* stream) {
 skv::RopeLaunch rope_launch(const skv::Geometry& g, skv::TokView src, skv::TokView dst, int32_t n_frames,
                             int64_t t0, int64_t clamp_max) {
   skv::RopeLaunch L;
-  L.src = src;
-  L.dst = dst;
+  L.job[0] = skv::RopeJob{src, dst, t0, (int32_t)clamp_max};
+  L.job[1] = L.job[2] = L.job[0];
+  L.njobs = 1;
   L.runs[0] = skv::FrameRun{0, n_frames, 0, 0};
   L.nruns = 1;
   L.n_frames = n_frames;
@@ -113,29 +114,23 @@ skv::RopeLaunch rope_launch(const skv::Geometry& g, skv::TokView src, skv::TokVi
   L.rope_h = g.rope_h;
   L.rope_w = g.rope_w;
   L.theta = g.theta;
-  L.t0 = t0;
-  L.clamp_max = clamp_max;
   L.dtype_bf16 = g.dtype == SKV_BF16;
   return L;
 }
 
 // Fused rotation before an attention pass: q at absolute ids (and at slot ids for REL sinks),
 // k_cur at absolute ids, into the workspace.
+// One launch: job 0 q at absolute ids, job 1 k_cur at absolute ids, job 2 (REL with sinks) q at slot ids.
 skv_status fused_prepare(skv_cache* c, const void* q, const void* k_cur, void* stream) {
   const skv::Geometry& g = c->g;
   const skv::VisiblePlan p = c->ring.plan(g, g.c);
   const int64_t T = c->ring.T;
-  skv_status st = launched(c, skv::launch_rope(rope_launch(g, token_view(g, q), token_view(g, ws_q_abs(c)), g.c, T, -1),
-                                               (hipStream_t)stream));
-  if (st != SKV_OK) return st;
-  if (g.mode == SKV_ROPE_REL && p.n_sink_vis > 0) {
-    st = launched(c, skv::launch_rope(rope_launch(g, token_view(g, q), token_view(g, ws_q_rel(c)), g.c,
-                                                  p.n_vis - g.c, g.W - 1),
-                                      (hipStream_t)stream));
-    if (st != SKV_OK) return st;
-  }
-  return launched(c, skv::launch_rope(rope_launch(g, token_view(g, k_cur), token_view(g, ws_k_cur(c)), g.c, T, -1),
-                                      (hipStream_t)stream));
+  skv::RopeLaunch L = rope_launch(g, token_view(g, q), token_view(g, ws_q_abs(c)), g.c, T, -1);
+  L.job[1] = skv::RopeJob{token_view(g, k_cur), token_view(g, ws_k_cur(c)), T, -1};
+  L.njobs = 2;
+  if (g.mode == SKV_ROPE_REL && p.n_sink_vis > 0)
+    L.job[L.njobs++] = skv::RopeJob{token_view(g, q), token_view(g, ws_q_rel(c)), p.n_vis - g.c, g.W - 1};
+  return launched(c, skv::launch_rope(L, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -276,27 +271,48 @@ skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int
   return SKV_OK;
 }
 
-skv_status rope_apply(const skv_cache* cc, const void* x_in, void* x_out, int32_t n_frames, int64_t start_frame,
-                      void* stream) {
+// rope_apply / rope_apply_qk: one launch over n (1 or 2) tensors with the same time ids.
+static skv_status rope_tensors(const skv_cache* cc, const void* const* in, void* const* out, int n, int32_t n_frames,
+                               int64_t start_frame, void* stream) {
   skv_cache* c = const_cast<skv_cache*>(cc);
   skv_status st = check_handle(c);
   if (st != SKV_OK) return st;
-  if ((st = check_ptr(x_in)) != SKV_OK) return st;
-  if ((st = check_ptr(x_out)) != SKV_OK) return st;
+  for (int i = 0; i < n; ++i) {
+    if ((st = check_ptr(in[i])) != SKV_OK) return st;
+    if ((st = check_ptr(out[i])) != SKV_OK) return st;
+  }
   const skv::Geometry& g = c->g;
   if (n_frames < 1 || (int64_t)n_frames * g.F > (int64_t)INT32_MAX / 2) return SKV_ERR_SHAPE;
-  skv::RopeLaunch L = rope_launch(g, token_view(g, x_in), token_view(g, x_out), n_frames, 0, -1);
+  int64_t t0;
+  int32_t clamp_max;
   if (g.mode == SKV_ROPE_ABS) {
     if (start_frame < 0) return SKV_ERR_SHAPE;
-    L.t0 = start_frame;
-    L.clamp_max = -1;
+    t0 = start_frame;
+    clamp_max = -1;
   } else {
     if (n_frames != g.c) return SKV_ERR_SHAPE;
     const skv::VisiblePlan p = c->ring.plan(g, g.c);
-    L.t0 = p.n_vis - g.c;
-    L.clamp_max = g.W - 1;
+    t0 = p.n_vis - g.c;
+    clamp_max = g.W - 1;
   }
+  skv::RopeLaunch L = rope_launch(g, token_view(g, in[0]), token_view(g, out[0]), n_frames, t0, clamp_max);
+  for (int i = 1; i < n; ++i) L.job[i] = skv::RopeJob{token_view(g, in[i]), token_view(g, out[i]), t0, clamp_max};
+  L.njobs = n;
   return launched(c, skv::launch_rope(L, (hipStream_t)stream));
+}
+
+skv_status rope_apply(const skv_cache* cache, const void* x_in, void* x_out, int32_t n_frames, int64_t start_frame,
+                      void* stream) {
+  const void* in[1] = {x_in};
+  void* out[1] = {x_out};
+  return rope_tensors(cache, in, out, 1, n_frames, start_frame, stream);
+}
+
+skv_status rope_apply_qk(const skv_cache* cache, const void* q_in, void* q_out, const void* k_in, void* k_out,
+                         int32_t n_frames, int64_t start_frame, void* stream) {
+  const void* in[2] = {q_in, k_in};
+  void* out[2] = {q_out, k_out};
+  return rope_tensors(cache, in, out, 2, n_frames, start_frame, stream);
 }
 
 skv_status rope_apply_window(skv_cache* c, void* stream) {

@@ -105,6 +105,15 @@ def test_init_validation_and_info():
     st, h = _init(LB480)
     assert skv.lib.rope_apply_window(h, nul) == skv.ERR_STATE              # abs mode has no window
     assert skv.lib.rope_apply(h, p, p, 4, -1, nul) == skv.ERR_SHAPE         # abs: start_frame >= 0
+    qk = skv.lib.rope_apply_qk
+    assert qk(h, p, p, p, p, 4, -1, nul) == skv.ERR_SHAPE
+    assert qk(h, p, p, nul, p, 4, 0, nul) == skv.ERR_NULL
+    assert qk(h, p, p, p, nul, 4, 0, nul) == skv.ERR_NULL
+    assert qk(h, p, ctypes.c_void_p(0x40008), p, p, 4, 0, nul) == skv.ERR_ALIGN
+    assert qk(h, p, p, p, p, 0, 0, nul) == skv.ERR_SHAPE
+    skv.lib.kv_cache_destroy(h)
+    st, h = _init(ABOT)
+    assert skv.lib.rope_apply_qk(h, p, p, p, p, 2, 0, nul) == skv.ERR_SHAPE   # rel: n_frames must equal c
     skv.lib.kv_cache_destroy(h)
 
 

@@ -108,6 +108,30 @@ def test_rope_abs(name, start):
     assert torch.equal(xd, got)
 
 
+@pytest.mark.parametrize("name", ["tiny", "small_abs", "small_rel", "small_f32_rel", "lb480", "abot720"])
+def test_rope_apply_qk_matches_two_calls(name):
+    """One launch over q and k gives exactly the bytes of two rope_apply calls (same ids, same math),
+    in place too; REL after a few appends so the chunk's slot ids are past the first frames."""
+    wl = WORKLOADS[name]
+    c = wl.cfg
+    say(f"[rope qk] {name}")
+    cache = skv.KVCache(c)
+    ro.prefill(wl, cache, None)
+    for ch in range(3):
+        cache.append_evict(ro.draw(wl, c.chunk_frames, ch, 4, si.K).cuda(), ro.draw(wl, c.chunk_frames, ch, 4, si.V).cuda())
+    start = cache.info().n_appended
+    q = ro.draw(wl, c.chunk_frames, 5, 0, si.Q).cuda()
+    k = ro.draw(wl, c.chunk_frames, 5, 0, si.K).cuda()
+    rq = cache.rope_apply(q, start_frame=start)
+    rk = cache.rope_apply(k, start_frame=start)
+    gq, gk = cache.rope_apply_qk(q, k, start_frame=start)
+    q2, k2 = q.clone(), k.clone()
+    cache.rope_apply_qk(q2, k2, q_out=q2, k_out=k2, start_frame=start)
+    torch.cuda.synchronize()
+    assert torch.equal(gq, rq) and torch.equal(gk, rk)
+    assert torch.equal(q2, rq) and torch.equal(k2, rk)
+
+
 @pytest.mark.parametrize("name", ["small_rel", "small_f32_rel", "abot720"])
 def test_rope_rel_and_window(name):
     wl = WORKLOADS[name]
