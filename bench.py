@@ -312,10 +312,9 @@ def guidance_leg(runner):
     outs = [torch.empty_like(q), torch.empty_like(q)]
     for _ in range(3):
         skv.chunk_attention_batch(caches, qs, ks, None, outs)
-    t = {}
-    for mode in ("batch", "single"):
-        evs = []
-        for _ in range(5):
+    evs = {"batch": [], "single": []}
+    for _ in range(6):   # the two modes interleaved, so that clock drift does not favour either
+        for mode in ("batch", "single"):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             if mode == "batch":
@@ -324,9 +323,9 @@ def guidance_leg(runner):
                 for i, cc in enumerate(caches):
                     cc.chunk_attention(qs[i], ks[i], None, out=outs[i])
             e1.record()
-            evs.append((e0, e1))
-        torch.cuda.synchronize()
-        t[mode] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+            evs[mode].append((e0, e1))
+    torch.cuda.synchronize()
+    t = {mode: float(np.mean([a.elapsed_time(b) for a, b in e])) for mode, e in evs.items()}
     n_vis = caches[0].info().n_vis
     flop = 2 * 4.0 * cfg.chunk_frames * f * n_vis * f * cfg.head_dim * cfg.heads
     return {"caches": 2, "n_vis": n_vis, "batch_ms": round(t["batch"], 4), "two_calls_ms": round(t["single"], 4),

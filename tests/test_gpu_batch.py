@@ -86,3 +86,36 @@ def test_guidance_batch_then_sampler():
     err = np.abs(x0.float().cpu().double().numpy() - ex0)
     # attention error (<= 2e-2 each) times 0.75 * (5 + 4), plus the bf16 rounding of x0
     assert err.max() <= 0.75 * 9 * 2e-2 + 2.0 ** -7 * np.abs(ex0).max(), err.max()
+
+
+@pytest.mark.parametrize("nb", [3, 4])
+def test_wide_batch(nb):
+    """Three and four caches (the batch limit) of 40 heads x 4 query tiles (160 four-wave workgroups
+    each, so four make a grid past one dispatch round): every element equals its single
+    chunk_attention call bit for bit, and element 0 matches the oracle."""
+    from streaming_kv_cache_amd.workloads import Workload
+    cfg = skv.Config(40, 128, 8, 16, 4, 1, 6, skv.ROPE_ABS, skv.BF16)
+    wl = Workload("batch_wide", cfg, n_chunks=3)
+    say(f"[batch split] nb={nb} heads={cfg.heads} lq={cfg.chunk_frames * cfg.tokens_per_frame}")
+    bases = tuple(100 * i for i in range(nb))
+    caches = [skv.KVCache(cfg) for _ in bases]
+    orc = ro.oracle_for(wl)
+    for ch in range(wl.n_chunks):
+        qr, kr, vd, raw0 = [], [], [], None
+        for cache, b in zip(caches, bases):
+            t = cache.info().n_appended
+            q, k, v = (ro.draw(wl, cfg.chunk_frames, ch, 0, tid, b) for tid in (si.Q, si.K, si.V))
+            if b == 0:
+                raw0 = (q, k, v)
+            rq, rk = cache.rope_apply_qk(q.cuda(), k.cuda(), start_frame=t)
+            qr.append(rq), kr.append(rk), vd.append(v.cuda())
+        outs = skv.chunk_attention_batch(caches, qr, kr, vd)
+        singles = [cache.chunk_attention(qr[i], kr[i], vd[i]) for i, cache in enumerate(caches)]
+        torch.cuda.synchronize()
+        for i in range(nb):
+            assert torch.equal(outs[i], singles[i]), f"chunk {ch} element {i}: batch != single"
+        ref = orc.chunk_attention(*(ro.f64(x) for x in raw0))
+        ro.assert_close(outs[0], ref, cfg.dtype, f"batch_wide chunk {ch} element 0")
+        for i, cache in enumerate(caches):
+            cache.append_evict(kr[i], vd[i])
+        orc.append(ro.f64(raw0[1]), ro.f64(raw0[2]))
