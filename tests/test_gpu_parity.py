@@ -189,6 +189,69 @@ def test_rollout_parity_kernel_shapes(name, waves, monkeypatch):
         ro.assert_close(out, ref, wl.cfg.dtype, f"{name} waves {waves} chunk {ch} pass {p}")
 
 
+def _edge_workloads():
+    from streaming_kv_cache_amd.workloads import Workload
+    C = skv.Config
+    return {
+        # one head, one-frame chunks, ring of two frames, relative ids
+        "edge_h1_c1_rel": Workload("edge_h1_c1_rel", C(1, 128, 3, 5, 1, 1, 3, skv.ROPE_REL, skv.BF16), n_chunks=7),
+        # one token per frame: every range start is unaligned (element-copy V path), one partial tile
+        "edge_f1_abs": Workload("edge_f1_abs", C(2, 64, 1, 1, 2, 1, 5, skv.ROPE_ABS, skv.BF16), n_chunks=8),
+        # W = S + c with relative ids: a chunk sees only the sinks and itself
+        "edge_rel_tight": Workload("edge_rel_tight", C(2, 128, 4, 4, 2, 2, 4, skv.ROPE_REL, skv.BF16), n_chunks=6),
+        # a chunk of 6 frames in a window of 7 without sinks: the ring wraps inside every append
+        "edge_bigc_nosink": Workload("edge_bigc_nosink", C(2, 128, 5, 7, 6, 0, 7, skv.ROPE_ABS, skv.BF16),
+                                     n_chunks=5),
+        # fp32, D = 32, one token per frame, no sinks, window 2, one-frame chunks
+        "edge_f1_f32_rel": Workload("edge_f1_f32_rel", C(1, 32, 1, 1, 1, 0, 2, skv.ROPE_REL, skv.F32), n_chunks=6),
+    }
+
+
+EDGE = list(_edge_workloads())
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("name", EDGE)
+def test_edge_shapes(name, waves, fused, monkeypatch):
+    """Degenerate shapes through every pass of a rollout against the oracle: both kernel shapes, the
+    pages' protocol and the fused rotation."""
+    wl = _edge_workloads()[name]
+    if wl.cfg.dtype == skv.F32 and waves == "8":
+        pytest.skip("one fp32 kernel shape")
+    monkeypatch.setenv("SKV_ATTN_WAVES", waves)
+    if fused:
+        wl = ro.fused(wl)
+    say(f"[edge] {name} waves={waves} fused={fused} chunks={wl.n_chunks}")
+    for ch, p, out, ref in ro.rollout(wl, wl.n_chunks):
+        torch.cuda.synchronize()
+        ro.assert_close(out, ref, wl.cfg.dtype, f"{name} chunk {ch} pass {p}")
+
+
+@pytest.mark.parametrize("name", EDGE)
+def test_edge_append_gather(name):
+    """Cache contents after every append equal the closed form bit for bit on the degenerate shapes."""
+    wl = _edge_workloads()[name]
+    c = wl.cfg
+    say(f"[edge gather] {name}")
+    cache = skv.KVCache(c)
+    hist_k, hist_v = [], []
+    for ch in range(wl.n_chunks + 2):
+        k = ro.draw(wl, c.chunk_frames, ch, 4, si.K)
+        v = ro.draw(wl, c.chunk_frames, ch, 4, si.V)
+        cache.append_evict(k.cuda(), v.cuda())
+        f = c.tokens_per_frame
+        hist_k += [k[i * f:(i + 1) * f] for i in range(c.chunk_frames)]
+        hist_v += [v[i * f:(i + 1) * f] for i in range(c.chunk_frames)]
+        t = len(hist_k)
+        keep = list(range(min(c.sink_frames, t))) + list(range(max(c.sink_frames, t - (c.window_frames - c.sink_frames)), t))
+        gk, gv, ids = cache.gather()
+        torch.cuda.synchronize()
+        assert list(ids) == keep
+        assert torch.equal(gk.cpu(), torch.cat([hist_k[i] for i in keep]))
+        assert torch.equal(gv.cpu(), torch.cat([hist_v[i] for i in keep]))
+
+
 def _probe_rollout(wl, mode):
     """q = 0 with one-hot (mode 'onehot') or random (mode 'zeroq') values: the answer is a plain mean."""
     c = wl.cfg
