@@ -118,9 +118,8 @@ skv::RopeLaunch rope_launch(const skv::Geometry& g, skv::TokView src, skv::TokVi
   return L;
 }
 
-// Fused rotation before an attention pass: q at absolute ids (and at slot ids for REL sinks),
-// k_cur at absolute ids, into the workspace.
-// One launch: job 0 q at absolute ids, job 1 k_cur at absolute ids, job 2 (REL with sinks) q at slot ids.
+// Fused rotation before an attention pass, into the workspace, in one launch: job 0 q at absolute
+// ids, job 1 k_cur at absolute ids, job 2 (REL with visible sinks) q at slot ids.
 skv_status fused_prepare(skv_cache* c, const void* q, const void* k_cur, void* stream) {
   const skv::Geometry& g = c->g;
   const skv::VisiblePlan p = c->ring.plan(g, g.c);
