@@ -106,8 +106,14 @@ const char* skv_status_string(skv_status s);
  * W*F*H*D elements of cfg->dtype) and for the workspace.  Physical layouts:
  *   K store  [H][W*F][D]   (head-major; slot s holds tokens [s*F, (s+1)*F));
  *   V store  [H][D][W*F]   (transposed per head, same token numbering);
- *   workspace: REL only, the rotated visible window [H][(W-c)*F][D], then the
- *   staged current-chunk values [H][D][P] with P = c*F rounded up to 64.
+ *   workspace: REL only, the rotated visible window [H][(W-c)*F][D] (with
+ *   fused_rope instead: q at absolute ids, k_cur at absolute ids and, REL, q at
+ *   slot ids, [c*F][H][D] each), then the staged current-chunk values [H][D][P]
+ *   with P = c*F rounded up to 64; then, for bf16 chunks whose attention grid
+ *   would fill less than half of the chip (few heads: e.g. one GPU's share of
+ *   a head-sharded model), at the next 256-byte boundary the fp32 partial
+ *   results of up to 16 key splits ([splits][c*F][H][D], then [splits][c*F][H][2]),
+ *   which chunk_attention merges.
  * Frame f < S lives in slot f, frame f >= S in slot S + (f-S) mod (W-S). */
 skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_t* workspace_bytes);
 

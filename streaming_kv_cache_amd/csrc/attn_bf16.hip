@@ -395,11 +395,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   // uniform (scalar branches on it) and known to be below NW
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
   const int l32 = lane & 31, hf = lane >> 5;
-  // every batch element has the same Lq and H
+  // every batch element has the same Lq, H and split count; split index slowest, so that the
+  // workgroups next to each other share the key range of their split
   const int n_qt = (ab.b[0].Lq + BM - 1) / BM;
   const int per = n_qt * ab.b[0].H;
-  const int tile = xcd_remap(blockIdx.x, per * ab.nb);
-  const int bi = tile / per, rest = tile - bi * per;
+  const int nsp = (!MASKED && ab.b[0].nsplit > 1) ? ab.b[0].nsplit : 1;
+  const int tile = xcd_remap(blockIdx.x, per * ab.nb * nsp);
+  const int sp = tile / (per * ab.nb), tl = tile - sp * per * ab.nb;
+  const int bi = tl / per, rest = tl - bi * per;
   const AttnArgs& a = ab.b[bi];
   const int h = rest / n_qt, qt = rest - h * n_qt;
   const int q_base = qt * BM + wave * 32;
@@ -419,7 +422,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
-  load_q(a.q);
   f32x16_t o[MBLK];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb)
@@ -482,6 +484,38 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     n_tiles += (seg_n(s_) + kBN - 1) / kBN;
   }
   if (n_tiles == 0) return;  // no keys: the host never launches this
+  // split keys: this workgroup's tiles [t_begin, t_begin + n_tiles) of the sequence
+  int t_begin = 0;
+  if (nsp > 1) {
+    t_begin = sp * a.split_tiles;
+    const int t_end = n_tiles < t_begin + a.split_tiles ? n_tiles : t_begin + a.split_tiles;
+    n_tiles = t_end - t_begin;
+    alt_tiles -= t_begin;  // local index of the query switch
+    if (n_tiles <= 0) {
+      // an empty split (a batch element with fewer tiles than the others): contributes nothing
+      const int qi = q_base + l32;
+      if (qi < a.Lq) {
+        const int64_t row = ((int64_t)sp * a.Lq + qi) * a.H + h;
+        float* po = a.part_o + row * D + 4 * hf;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) *(f32x4_t*)(po + 32 * mb + 8 * g) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (hf == 0) {
+          a.part_ml[2 * row] = -INFINITY;
+          a.part_ml[2 * row + 1] = 0.f;
+        }
+      }
+      return;
+    }
+  }
+  // queries of the first tile (from the switch on: at q_alt)
+  if (alt_tiles <= 0) {
+    load_q(a.q_alt);
+    alt_tiles = 1 << 30;
+  } else {
+    load_q(a.q);
+  }
   int ksi = 0, krem = 0, k_rs_b = 0;
   const uint8_t* kp = nullptr;
   
@@ -528,6 +562,26 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   while (krem <= 0 && ++ksi < nseg) k_seg(ksi);
   v_seg(0);
   while (vrem <= 0 && ++vsi < nseg) v_seg(vsi);
+  // split keys: move both iterators (they walk the same ranges) to tile t_begin
+  for (int skip = t_begin; skip > 0;) {
+    const int left = (krem + kBN - 1) / kBN;  // tiles left in the current range
+    if (left <= 0) break;                       // no range left (cannot happen: t_begin < tiles)
+    if (skip < left) {
+      k_so += skip * kBN * k_rs_b;
+      kkey += skip * kBN;
+      krem -= skip * kBN;
+      v_so += skip * 2 * kBN;
+      vp += skip * 2 * kBN;
+      vrem -= skip * kBN;
+      skip = 0;
+    } else {
+      skip -= left;
+      krem = 0;
+      vrem = 0;
+      while (krem <= 0 && ++ksi < nseg) k_seg(ksi);
+      while (vrem <= 0 && ++vsi < nseg) v_seg(vsi);
+    }
+  }
 
   // Issue the next K tile into stage st; returns its valid key count (and, masked, the
   // sequence index of its first key in key0).
@@ -833,8 +887,26 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[(stp - 2) * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
   }
 
-  const float inv = 1.f / half_swap_sum(l_run);
+  const float l_row = half_swap_sum(l_run);
   const int qi = q_base + l32;
+  if (nsp > 1) {
+    // split keys: unnormalised O, running max and row sum of this split for the merge pass
+    if (qi < a.Lq) {
+      const int64_t row = ((int64_t)sp * a.Lq + qi) * a.H + h;
+      float* po = a.part_o + row * D + 4 * hf;
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4_t*)(po + 32 * mb + 8 * g) = f32x4_t{o[mb][4 * g], o[mb][4 * g + 1], o[mb][4 * g + 2], o[mb][4 * g + 3]};
+      if (hf == 0) {
+        a.part_ml[2 * row] = m_run;
+        a.part_ml[2 * row + 1] = l_row;
+      }
+    }
+    return;
+  }
+  const float inv = 1.f / l_row;
   if (qi < a.Lq) {
     uint16_t* op = (uint16_t*)a.out + ((int64_t)qi * a.H + h) * D + 4 * hf;
 #pragma unroll
@@ -848,21 +920,80 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   }
 }
 
+// Split keys: merge the partial results of nsplit key ranges into out (bf16).  Thread i handles
+// row r = i / (D / 4) of the [Lq * H] rows and its dims 4 (i % (D / 4)) .. +3:
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s (empty splits: m = -inf).
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* part_o, const float* part_ml, int nsplit,
+                                                         int64_t rows, int D, uint16_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q4 = D / 4;
+  if (i >= rows * q4) return;
+  const int64_t r = i / q4;
+  const int d = 4 * (int)(i - r * q4);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[2 * (s * rows + r)]);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float m = part_ml[2 * (s * rows + r)];
+    if (m == -INFINITY) continue;
+    const float w = __builtin_amdgcn_exp2f(m - M);
+    L += w * part_ml[2 * (s * rows + r) + 1];
+    const f32x4_t o = *(const f32x4_t*)(part_o + (s * rows + r) * D + d);
+    acc += w * o;
+  }
+  const float inv = 1.f / L;
+  *(u32x2_t*)(out + r * D + d) = u32x2_t{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+}
+
 // Two shapes of the same kernel: 4 waves x 32 queries with two stages (two workgroups per CU),
 // or 8 waves x 32 queries with four stages (one workgroup per CU; each K/V tile feeds twice the
 // queries and loads run two tiles ahead).  The larger one runs about 10% faster per query once
 // the grid fills the chip; with few query tiles its coarser grid leaves CUs idle, so pick by
-// the number of dispatch rounds each needs on 256 CUs.
+// the number of dispatch rounds each needs on 256 CUs.  A grid that fills less than half of one
+// round (few heads, e.g. one GPU's share of a head-sharded model) has its keys split so that the
+// chip fills, when the caller's workspace holds the partial results.
 template <bool MASKED>
-static hipError_t launch_vt(const AttnBatch& a, int D, hipStream_t stream) {
+static hipError_t launch_vt(const AttnBatch& in, int D, hipStream_t stream) {
+  AttnBatch a = in;
   const AttnArgs& a0 = a.b[0];
   const int64_t wg4 = (int64_t)((a0.Lq + 127) / 128) * a0.H * a.nb, wg8 = (int64_t)((a0.Lq + 255) / 256) * a0.H * a.nb;
   const double rounds4 = (double)((wg4 + 511) / 512), rounds8 = 0.9 * (double)((wg8 + 255) / 256);
   // SKV_ATTN_WAVES=4 or 8 forces one shape (tests cover both on small inputs)
   const char* env = std::getenv("SKV_ATTN_WAVES");
-  const int forced = env ? std::atoi(env) : 0;
+  const int forced = (env && *env) ? std::atoi(env) : 0;
   const bool big = forced == 8 || (forced != 4 && rounds8 < rounds4);
-  const dim3 grid((unsigned)(big ? wg8 : wg4));
+  const int64_t wg = big ? wg8 : wg4, slots = big ? 256 : 512;
+  // split keys: SKV_ATTN_SPLIT=0 never, =1 whenever the buffers allow (tests), unset: small grids
+  int nsplit = 1;
+  if (!MASKED) {
+    const char* se = std::getenv("SKV_ATTN_SPLIT");
+    const int mode = (se && *se) ? std::atoi(se) : -1;
+    int cap = 1 << 30, max_tiles = 0;
+    for (int i = 0; i < a.nb; ++i) {
+      cap = a.b[i].split_cap < cap ? a.b[i].split_cap : cap;
+      int nt = 0;
+      for (int s_ = 0; s_ < a.b[i].nseg; ++s_) nt += (a.b[i].seg[s_].n + kBN - 1) / kBN;
+      max_tiles = nt > max_tiles ? nt : max_tiles;
+    }
+    if (mode != 0 && cap > 1 && (mode == 1 || 2 * wg <= slots)) {
+      int want = (int)(slots / wg);  // whole grid within one round
+      if (mode == 1 && want < 2) want = 2;
+      nsplit = want < cap ? want : cap;
+      nsplit = nsplit < max_tiles ? nsplit : max_tiles;
+    }
+    if (nsplit > 1) {
+      for (int i = 0; i < a.nb; ++i) {
+        int nt = 0;
+        for (int s_ = 0; s_ < a.b[i].nseg; ++s_) nt += (a.b[i].seg[s_].n + kBN - 1) / kBN;
+        a.b[i].nsplit = nsplit;
+        a.b[i].split_tiles = (nt + nsplit - 1) / nsplit;
+      }
+    } else {
+      for (int i = 0; i < a.nb; ++i) a.b[i].nsplit = 1;
+    }
+  }
+  const dim3 grid((unsigned)(wg * nsplit));
   switch (D * (big ? -1 : 1)) {
     case 64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 4, 2, MASKED>), grid, dim3(256), 0, stream, a); break;
     case 128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 4, 2, MASKED>), grid, dim3(256), 0, stream, a); break;
@@ -870,7 +1001,17 @@ static hipError_t launch_vt(const AttnBatch& a, int D, hipStream_t stream) {
     case -128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 8, 4, MASKED>), grid, dim3(512), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit <= 1) return e;
+  for (int i = 0; i < a.nb && e == hipSuccess; ++i) {
+    const int64_t rows = (int64_t)a.b[i].Lq * a.b[i].H;
+    const int64_t threads = rows * (D / 4);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)a.b[i].part_o, (const float*)a.b[i].part_ml, nsplit, rows, D,
+                       (uint16_t*)a.b[i].out);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_attention_bf16_vt(const AttnBatch& a, int D, hipStream_t stream) { return launch_vt<false>(a, D, stream); }

@@ -65,6 +65,15 @@ struct AttnArgs {
   // frames of mF tokens, query frames from mq0 in chunks of mc frames, mS sinks, window mW;
   // seg[0] then describes the keys / V^T of the whole sequence
   int32_t mF, mq0, mc, mS, mW;
+  // split keys (unmasked kernel): nsplit workgroups per query tile, split s taking tiles
+  // [s * split_tiles, (s + 1) * split_tiles) of the key sequence, write instead of out the
+  // unnormalised O to part_o [nsplit][Lq][H][D] and (running max in log2 units, row sum) to
+  // part_ml [nsplit][Lq][H][2]; a merge pass combines them.  nsplit <= 1: no split.  split_cap:
+  // the most splits the part buffers hold (set by the host; 0: never split).
+  float* part_o;
+  float* part_ml;
+  int32_t split_cap;
+  int32_t nsplit, split_tiles;
 };
 
 // Up to kMaxAttnBatch independent attention problems of one shape (same Lq, H, D) in one

@@ -71,6 +71,20 @@ int64_t ws_fused_elems(const skv::Geometry& g) {
 int64_t ws_total_elems(const skv::Geometry& g) {
   return ws_window_elems(g) + ws_fused_elems(g) + (int64_t)g.H * g.D * cur_row(g);
 }
+// Split keys (bf16, a chunk grid that fills less than half a dispatch round, e.g. few heads):
+// up to split_cap partial results per query row after the other parts, at a 256-byte boundary:
+// part_o [cap][c*F][H][D] fp32, then part_ml [cap][c*F][H][2] fp32.
+int32_t split_cap(const skv::Geometry& g) {
+  if (g.dtype != SKV_BF16) return 0;
+  const int64_t wg4 = ((int64_t)g.c * g.F + 127) / 128 * g.H;  // 4-wave workgroups of one chunk
+  if (2 * wg4 > 512) return 0;
+  const int64_t cap = 512 / wg4;
+  return (int32_t)(cap < 16 ? cap : 16);
+}
+int64_t ws_split_off(const skv::Geometry& g) { return (ws_total_elems(g) * g.elt + 255) / 256 * 256; }
+int64_t ws_split_bytes(const skv::Geometry& g) {
+  return (int64_t)split_cap(g) * g.c * g.F * g.H * (g.D + 2) * 4;
+}
 void* ws_q_abs(const skv_cache* c) { return (char*)c->ws + ws_window_elems(c->g) * c->g.elt; }
 void* ws_k_cur(const skv_cache* c) { return (char*)ws_q_abs(c) + chunk_elems(c->g) * c->g.elt; }
 void* ws_q_rel(const skv_cache* c) { return (char*)ws_k_cur(c) + chunk_elems(c->g) * c->g.elt; }
@@ -168,7 +182,7 @@ skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_
   skv_status st = skv::make_geometry(cfg, &g);
   if (st != SKV_OK) return st;
   *store_bytes_each = (size_t)skv::store_elems(g) * g.elt;
-  *workspace_bytes = (size_t)ws_total_elems(g) * g.elt;
+  *workspace_bytes = (size_t)(ws_split_off(g) + ws_split_bytes(g));
   return SKV_OK;
 }
 
@@ -367,6 +381,12 @@ static skv_status attention_args(skv_cache* c, const void* q, const void* k_cur,
   a->H = g.H;
   a->sl2 = softmax_scale_log2(g.D);
   a->nseg = 0;
+  a->split_cap = split_cap(g);
+  if (a->split_cap > 1) {
+    char* base = (char*)c->ws + ws_split_off(g);
+    a->part_o = (float*)base;
+    a->part_ml = (float*)(base + (int64_t)a->split_cap * g.c * g.F * g.H * g.D * 4);
+  }
   const int64_t store_hs = (int64_t)g.W * g.F * g.D;
   const int64_t ws_hs = (int64_t)(g.W - g.c) * g.F * g.D;
   const int per16 = 16 / g.elt;

@@ -57,6 +57,12 @@ WORKLOADS = {
     # 40 layers of the 480P layer, cross attention to 512 cached text tokens, 300 chunks
     "fulldepth480": Workload("fulldepth480", Config(40, 128, 30, 52, 4, 6, 18, ROPE_ABS, BF16), n_chunks=300,
                              text_tokens=512, layers=40, steady_chunk=4, timesteps=LINGBOT_STEPS),
+    # one GPU's share of a model sharded by heads over 8 GPUs (ABot 24 / 8 = 3 heads, LingBot 40 / 8 = 5):
+    # the real per-GPU shape, whose attention grid alone leaves most of the chip idle
+    "abot720_h3": Workload("abot720_h3", Config(3, 128, 22, 40, 3, 5, 21, ROPE_REL, BF16), n_chunks=40,
+                           prefill=5, steady_chunk=5, timesteps=ABOT_STEPS),
+    "lb480_h5": Workload("lb480_h5", Config(5, 128, 30, 52, 4, 6, 18, ROPE_ABS, BF16), n_chunks=22,
+                         steady_chunk=4, timesteps=LINGBOT_STEPS),
     # small shapes: several 64-key tiles, ragged frame sizes, ring wrap-around
     "small_abs": Workload("small_abs", Config(3, 128, 7, 9, 2, 2, 7, ROPE_ABS, BF16), n_chunks=12, steady_chunk=3),
     "small_rel": Workload("small_rel", Config(3, 128, 5, 13, 3, 2, 9, ROPE_REL, BF16), n_chunks=10, prefill=2,

@@ -49,6 +49,16 @@ def test_cache_bytes():
     assert store == 18 * 1560 * 40 * 128 * 2 and ws == 40 * 128 * pad64(4 * 1560) * 2
     tiny = skv.Config(2, 64, 4, 4, 2, 1, 4, dtype=skv.F32)
     assert skv.cache_bytes(tiny) == (4 * 16 * 2 * 64 * 4, 2 * 64 * 64 * 4)
+    # 3 heads of 480P: 49 query tiles x 3 heads = 147 four-wave workgroups fill less than half of
+    # the 512 slots, so the workspace also holds floor(512 / 147) = 3 key splits of fp32 partials
+    lb_h3 = skv.Config(3, 128, 30, 52, 4, 6, 18)
+    base = 3 * 128 * pad64(4 * 1560) * 2
+    store, ws = skv.cache_bytes(lb_h3)
+    assert ws == (base + 255) // 256 * 256 + 3 * 4 * 1560 * 3 * (128 + 2) * 4
+    # small grids: at most 16 splits
+    small = skv.Config(3, 128, 5, 13, 3, 2, 9, rope_mode=skv.ROPE_REL)
+    base = (9 - 3) * 65 * 3 * 128 * 2 + 3 * 128 * pad64(3 * 65) * 2
+    assert skv.cache_bytes(small)[1] == (base + 255) // 256 * 256 + 16 * 3 * 65 * 3 * (128 + 2) * 4
 
 
 @pytest.mark.parametrize("bad", [

@@ -25,6 +25,8 @@ def say(msg):
 @pytest.mark.parametrize("name", ["small_abs", "small_rel", "small_f32_rel"])
 def test_guidance_batch(name, waves, monkeypatch):
     monkeypatch.setenv("SKV_ATTN_WAVES", waves)
+    # bit-equality with single calls needs the same key split: a batch's grid may choose another
+    monkeypatch.setenv("SKV_ATTN_SPLIT", "0")
     wl = WORKLOADS[name]
     cfg = wl.cfg
     bases = (0, 500)
@@ -89,11 +91,12 @@ def test_guidance_batch_then_sampler():
 
 
 @pytest.mark.parametrize("nb", [3, 4])
-def test_wide_batch(nb):
+def test_wide_batch(nb, monkeypatch):
     """Three and four caches (the batch limit) of 40 heads x 4 query tiles (160 four-wave workgroups
     each, so four make a grid past one dispatch round): every element equals its single
     chunk_attention call bit for bit, and element 0 matches the oracle."""
     from streaming_kv_cache_amd.workloads import Workload
+    monkeypatch.setenv("SKV_ATTN_SPLIT", "0")   # bit-equality with single calls: same (no) key split
     cfg = skv.Config(40, 128, 8, 16, 4, 1, 6, skv.ROPE_ABS, skv.BF16)
     wl = Workload("batch_wide", cfg, n_chunks=3)
     say(f"[batch split] nb={nb} heads={cfg.heads} lq={cfg.chunk_frames * cfg.tokens_per_frame}")
@@ -119,3 +122,36 @@ def test_wide_batch(nb):
         for i, cache in enumerate(caches):
             cache.append_evict(kr[i], vd[i])
         orc.append(ro.f64(raw0[1]), ro.f64(raw0[2]))
+
+
+@pytest.mark.parametrize("name", ["small_abs", "small_rel"])
+def test_guidance_batch_split(name):
+    """With key splits (the default for these small grids) the batch still matches the oracle."""
+    wl = WORKLOADS[name]
+    cfg = wl.cfg
+    bases = (0, 500)
+    caches = [skv.KVCache(cfg) for _ in bases]
+    orcs = [ro.oracle_for(wl) for _ in bases]
+    for cache, orc, b in zip(caches, orcs, bases):
+        ro.prefill(wl, cache, orc, b)
+    say(f"[batch split] {name}")
+    for ch in range(wl.n_chunks):
+        if cfg.rope_mode == skv.ROPE_REL:
+            for cache in caches:
+                cache.rope_apply_window()
+        qs, ks, vs, qr, kr = [], [], [], [], []
+        for cache, b in zip(caches, bases):
+            t = cache.info().n_appended
+            q, k, v = (ro.draw(wl, cfg.chunk_frames, ch, ro.WRITE_BACK, tid, b) for tid in (si.Q, si.K, si.V))
+            qs.append(q), ks.append(k), vs.append(v)
+            a, bk = cache.rope_apply_qk(q.cuda(), k.cuda(), start_frame=t)
+            qr.append(a), kr.append(bk)
+        vd = [v.cuda() for v in vs]
+        outs = skv.chunk_attention_batch(caches, qr, kr, vd)
+        torch.cuda.synchronize()
+        for i in range(2):
+            ref = orcs[i].chunk_attention(ro.f64(qs[i]), ro.f64(ks[i]), ro.f64(vs[i]))
+            ro.assert_close(outs[i], ref, cfg.dtype, f"{name} chunk {ch} element {i}")
+        for i, cache in enumerate(caches):
+            cache.append_evict(kr[i] if cfg.rope_mode == skv.ROPE_ABS else ks[i].cuda(), vd[i])
+            orcs[i].append(ro.f64(ks[i]), ro.f64(vs[i]))

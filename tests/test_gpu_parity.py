@@ -177,13 +177,19 @@ def test_rollout_parity(name):
     say(f"  worst max/mean/relrms = {worst}")
 
 
+@pytest.mark.parametrize("split", ["0", "auto"])
 @pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("name", ["small_abs", "small_rel", "small_d64", "small_nosink"])
-def test_rollout_parity_kernel_shapes(name, waves, monkeypatch):
-    """Both bf16 kernel shapes (4 waves / two stages, 8 waves / four stages) on the same rollouts."""
+def test_rollout_parity_kernel_shapes(name, waves, split, monkeypatch):
+    """Both bf16 kernel shapes (4 waves / two stages, 8 waves / four stages) on the same rollouts,
+    with the keys split over workgroups (the default for these small grids) and without."""
     monkeypatch.setenv("SKV_ATTN_WAVES", waves)
+    if split == "0":
+        monkeypatch.setenv("SKV_ATTN_SPLIT", "0")
+    else:
+        monkeypatch.delenv("SKV_ATTN_SPLIT", raising=False)
     wl = WORKLOADS[name]
-    say(f"[rollout] {name} waves={waves} chunks={wl.n_chunks}")
+    say(f"[rollout] {name} waves={waves} split={split} chunks={wl.n_chunks}")
     for ch, p, out, ref in ro.rollout(wl, wl.n_chunks):
         torch.cuda.synchronize()
         ro.assert_close(out, ref, wl.cfg.dtype, f"{name} waves {waves} chunk {ch} pass {p}")
@@ -401,7 +407,7 @@ def _rows(lq, n=48, seed=0):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["abot720", "lb480", "lb720"])
+@pytest.mark.parametrize("name", ["abot720", "lb480", "lb720", "abot720_h3", "lb480_h5"])
 def test_full_size_sampled(name):
     """Roll out to the first steady chunk and one past it; compare sampled query rows (all heads)."""
     wl = WORKLOADS[name]
@@ -419,6 +425,38 @@ def test_full_size_sampled(name):
         say(f"  chunk {ch} pass {p}: max {e[0]:.3g} mean {e[1]:.3g} relrms {e[2]:.3g}")
         checked += 1
     assert checked == 6
+
+
+@pytest.mark.parametrize("name", ["abot720_h3", "lb480_h5"])
+def test_split_matches_unsplit(name, monkeypatch):
+    """One GPU's share of a head-sharded model (ABot 3 of 24 heads, LingBot 480P 5 of 40): the key
+    split the small grid takes agrees with the unsplit kernel on every row (the two differ only in
+    summation order), and the split path is the one taken by default."""
+    wl = WORKLOADS[name]
+    c = wl.cfg
+    say(f"[split] {name}")
+    cache = skv.KVCache(c)
+    ro.prefill(wl, cache, None)
+    while cache.info().n_vis < c.window_frames:
+        k = ro.draw(wl, c.chunk_frames, 0, 4, si.K).cuda()
+        cache.append_evict(k if c.rope_mode == skv.ROPE_REL else cache.rope_apply(k, start_frame=cache.info().n_appended),
+                           ro.draw(wl, c.chunk_frames, 0, 4, si.V).cuda())
+    if c.rope_mode == skv.ROPE_REL:
+        cache.rope_apply_window()
+    t = cache.info().n_appended
+    q, k = cache.rope_apply_qk(ro.draw(wl, c.chunk_frames, 1, 0, si.Q).cuda(), ro.draw(wl, c.chunk_frames, 1, 0, si.K).cuda(),
+                               start_frame=t)
+    v = ro.draw(wl, c.chunk_frames, 1, 0, si.V).cuda()
+    monkeypatch.delenv("SKV_ATTN_SPLIT", raising=False)
+    split = cache.chunk_attention(q, k, v)
+    monkeypatch.setenv("SKV_ATTN_SPLIT", "0")
+    whole = cache.chunk_attention(q, k, v)
+    torch.cuda.synchronize()
+    e = ro.errors(split, whole.float().cpu().double().numpy())
+    say(f"  split vs unsplit: max {e[0]:.3g} mean {e[1]:.3g} relrms {e[2]:.3g}")
+    # both outputs are bf16 roundings (relative error <= 2^-9 each) of sums whose P were rounded to
+    # bf16 against different running maxima: they may differ by 2^-8 relative
+    assert e[0] <= 2 ** -7 and e[2] <= 2 ** -8
 
 
 def test_staged_v_matches_direct():
