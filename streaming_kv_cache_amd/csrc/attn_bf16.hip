@@ -962,9 +962,9 @@ static hipError_t launch_vt(const AttnBatch& in, int D, hipStream_t stream) {
   // SKV_ATTN_WAVES=4 or 8 forces one shape (tests cover both on small inputs)
   const char* env = std::getenv("SKV_ATTN_WAVES");
   const int forced = (env && *env) ? std::atoi(env) : 0;
-  const bool big = forced == 8 || (forced != 4 && rounds8 < rounds4);
-  const int64_t wg = big ? wg8 : wg4, slots = big ? 256 : 512;
-  // split keys: SKV_ATTN_SPLIT=0 never, =1 whenever the buffers allow (tests), unset: small grids
+  bool big = forced == 8 || (forced != 4 && rounds8 < rounds4);
+  // split keys: SKV_ATTN_SPLIT=0 never, =1 whenever the buffers allow (tests), unset: grids that fill
+  // at most half of one dispatch round
   int nsplit = 1;
   if (!MASKED) {
     const char* se = std::getenv("SKV_ATTN_SPLIT");
@@ -976,12 +976,19 @@ static hipError_t launch_vt(const AttnBatch& in, int D, hipStream_t stream) {
       for (int s_ = 0; s_ < a.b[i].nseg; ++s_) nt += (a.b[i].seg[s_].n + kBN - 1) / kBN;
       max_tiles = nt > max_tiles ? nt : max_tiles;
     }
-    if (mode != 0 && cap > 1 && (mode == 1 || 2 * wg <= slots)) {
-      int want = (int)(slots / wg);  // whole grid within one round
+    // splits a shape would take: as many as fit the grid into one round
+    auto splits = [&](int64_t wgs, int64_t slots) -> int {
+      if (mode == 0 || cap <= 1 || (mode != 1 && 2 * wgs > slots)) return 1;
+      int want = (int)(slots / wgs);
       if (mode == 1 && want < 2) want = 2;
-      nsplit = want < cap ? want : cap;
-      nsplit = nsplit < max_tiles ? nsplit : max_tiles;
-    }
+      want = want < cap ? want : cap;
+      return want < max_tiles ? want : max_tiles;
+    };
+    const int s4 = splits(wg4, 512), s8 = splits(wg8, 256);
+    // both shapes fit one round once split: take the one whose split grid fills more of the chip
+    // (equal fill: the 8-wave shape, faster per tile)
+    if (!forced && (s4 > 1 || s8 > 1)) big = (double)(wg8 * s8) / 256.0 >= (double)(wg4 * s4) / 512.0;
+    nsplit = big ? s8 : s4;
     if (nsplit > 1) {
       for (int i = 0; i < a.nb; ++i) {
         int nt = 0;
@@ -993,6 +1000,7 @@ static hipError_t launch_vt(const AttnBatch& in, int D, hipStream_t stream) {
       for (int i = 0; i < a.nb; ++i) a.b[i].nsplit = 1;
     }
   }
+  const int64_t wg = big ? wg8 : wg4;
   const dim3 grid((unsigned)(wg * nsplit));
   switch (D * (big ? -1 : 1)) {
     case 64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 4, 2, MASKED>), grid, dim3(256), 0, stream, a); break;
