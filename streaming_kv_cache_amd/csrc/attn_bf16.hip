@@ -15,7 +15,10 @@
 //     x 32 rows with four stages (one workgroup per CU); the host picks the one
 //     that needs fewer dispatch rounds;
 //   * attn_bf16_tokv_kernel (cross attention over caller-provided token-major V):
-//     tiles staged through registers, V transposed on its way into LDS.
+//     tiles staged through registers, V transposed on its way into LDS;
+//   * attn_merge_kernel: when a grid would leave most of the chip idle (few heads), the
+//     cache-path kernel splits each query tile's keys over several workgroups, which write
+//     partial (O, running max, row sum); this pass combines them (log-sum-exp weights).
 //
 // Work decomposition (wave64, gfx950):
 //   * a workgroup owns the query rows of its waves for one head; workgroup ids are
