@@ -178,7 +178,12 @@ skv_status kv_cache_stage_v(skv_cache* cache, const void* v_cur, int32_t n_frame
  * equal c.  REL mode with cached history requires rope_apply_window first.
  * bf16 runs one of two kernel shapes (4 or 8 waves per workgroup), chosen from
  * the grid size; the environment variable SKV_ATTN_WAVES=4 or 8, read at each
- * call, forces one of them (the two may round differently). */
+ * call, forces one of them (the two may round differently).  A bf16 grid that
+ * would fill at most half of the chip (few heads, e.g. one GPU's share of a
+ * head-sharded model) has each query tile's keys split over several
+ * workgroups, whose partial results (in the workspace) a second kernel merges
+ * on the same stream; SKV_ATTN_SPLIT=0 disables that, =1 splits whenever the
+ * workspace has room (results differ from the unsplit ones by rounding only). */
 skv_status chunk_attention(const skv_cache* cache, const void* q, const void* k_cur, const void* v_cur,
                            int32_t n_frames, void* out, void* stream);
 
