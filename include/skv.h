@@ -106,7 +106,7 @@ const char* skv_status_string(skv_status s);
  * W*F*H*D elements of cfg->dtype) and for the workspace.  Physical layouts:
  *   K store  [H][W*F][D]   (head-major; slot s holds tokens [s*F, (s+1)*F));
  *   V store  [H][D][W*F]   (transposed per head, same token numbering);
- *   workspace: REL only, the rotated visible window [H][(W-c)*F][D] (with
+ *   workspace: first (REL only) the rotated visible window [H][(W-c)*F][D] (with
  *   fused_rope instead: q at absolute ids, k_cur at absolute ids and, REL, q at
  *   slot ids, [c*F][H][D] each), then the staged current-chunk values [H][D][P]
  *   with P = c*F rounded up to 64; then, for bf16 chunks whose attention grid
@@ -117,9 +117,9 @@ const char* skv_status_string(skv_status s);
  * Frame f < S lives in slot f, frame f >= S in slot S + (f-S) mod (W-S). */
 skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_t* workspace_bytes);
 
-/* Bind caller-allocated stores (and, in REL mode, the workspace) to a new
- * handle with zero frames appended ([ABot-stream] reset_stream()).  The device
- * memory is not touched.  *out receives the handle. */
+/* Bind caller-allocated stores and workspace (kv_cache_bytes gives the sizes) to
+ * a new handle with zero frames appended ([ABot-stream] reset_stream()).  The
+ * device memory is not touched.  *out receives the handle. */
 skv_status kv_cache_init(const skv_config* cfg, void* k_store, void* v_store, void* workspace,
                          skv_cache** out);
 
