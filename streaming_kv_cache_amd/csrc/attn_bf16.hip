@@ -375,7 +375,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
 __device__ __forceinline__ float half_swap_max(float x) { return fmaxf(x, xor32(x)); }
 __device__ __forceinline__ float half_swap_sum(float x) { return x + xor32(x); }
 
-template <int D, int NW, int NSTAGE, bool MASKED>
+// FOLLOW (masked only): the running max follows every half tile from -inf, for rows that may see no
+// key of the first tiles (no sinks).  With sinks every row sees key 0 of its workgroup's first tile,
+// so the max starts there and is raised only on overflow, as unmasked.
+template <int D, int NW, int NSTAGE, bool MASKED, bool FOLLOW = MASKED>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(AttnBatch ab) {
   static_assert(NSTAGE == 2 || NSTAGE == 4, "two or four stages");
   constexpr int BM = NW * 32;
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
   // unmasked: the running max starts at the first half tile's max; masked: at -inf (a row may
   // see no key of the first tiles) and follows every half tile's max
-  float m_run = MASKED ? -INFINITY : 0.f, l_run = 0.f;
+  float m_run = FOLLOW ? -INFINITY : 0.f, l_run = 0.f;
   // unmasked: -m_run in every entry, the accumulator the score products start from, so the
   // scores come out already relative to the running max (no subtraction per score)
   f32x16_t negm;
@@ -615,7 +618,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       }
     }
     krem -= kBN;
-    kp += kBN * k_rs_b;
     k_so += kBN * k_rs_b;
     while (krem <= 0 && ++ksi < nseg) k_seg(ksi);
     return nk;
@@ -776,15 +778,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = ld_bf16x8(kt + koff[0] + 32 * ks);
     __builtin_amdgcn_sched_barrier(0);
     f32x16_t s0 = negm;
-    if constexpr (MASKED) s0 = f32x16_t{};
+    if constexpr (FOLLOW) s0 = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s0, 0, 0, 0);
-    float sub0;
-    if constexpr (MASKED) {
-      mask_half(s0, k0, nk);
+    float sub0 = 0.f;
+    if constexpr (MASKED) mask_half(s0, k0, nk);
+    if constexpr (FOLLOW) {
       sub0 = follow_max(s0);
     } else {
-      if (nk < 32) {
+      if (!MASKED && nk < 32) {
         int nkh = nk - 8 * hf;  // key score_key(r, hf) >= nk  <=>  score_key(r, 0) >= nk - 8 hf
         asm volatile("" : "+v"(nkh));
 #pragma unroll
@@ -805,7 +807,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 
     // ---- keys 32..63 on the matrix cores while P of keys 0..31 is formed
     f32x16_t s1 = negm;
-    if constexpr (MASKED) s1 = f32x16_t{};
+    if constexpr (FOLLOW) s1 = f32x16_t{};
     bf16x8_t pb[4];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = ld_bf16x8(kt + koff[1] + 32 * ks);
@@ -820,7 +822,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     }
     // The running max is raised only when some score exceeds it by a lot (a row sum past
     // 2^60): the result is the same for any max, and P stays far below overflow.
-    if (!MASKED && __any(lsum > 0x1p60f)) {
+    if (!FOLLOW && __any(lsum > 0x1p60f)) {
       // scores are relative to the old max (s1 too, its product started from the old -m_run)
       const float up = fmaxf(max_half(s0), 0.f);
       raise_by(up);
@@ -856,7 +858,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 #pragma unroll
       for (int mb = 0; mb < MBLK; ++mb)
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[stp * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
-    if constexpr (MASKED) {
+    if constexpr (FOLLOW) {
       lsum = exp_half(s1, follow_max(s1), pb[2], pb[3]);
     } else {
       lsum = exp_half(s1, 0.f, pb[2], pb[3]);
@@ -1005,12 +1007,25 @@ static hipError_t launch_vt(const AttnBatch& in, int D, hipStream_t stream) {
   }
   const int64_t wg = big ? wg8 : wg4;
   const dim3 grid((unsigned)(wg * nsplit));
-  switch (D * (big ? -1 : 1)) {
-    case 64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 4, 2, MASKED>), grid, dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 4, 2, MASKED>), grid, dim3(256), 0, stream, a); break;
-    case -64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 8, 4, MASKED>), grid, dim3(512), 0, stream, a); break;
-    case -128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 8, 4, MASKED>), grid, dim3(512), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+  // masked with sinks: every row sees key 0, so the running max need not follow every half tile
+  const bool follow = MASKED && a0.mS == 0;
+  const int key = D * (big ? -1 : 1);
+  if (!follow) {
+    switch (key) {
+      case 64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 4, 2, MASKED, false>), grid, dim3(256), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 4, 2, MASKED, false>), grid, dim3(256), 0, stream, a); break;
+      case -64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 8, 4, MASKED, false>), grid, dim3(512), 0, stream, a); break;
+      case -128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 8, 4, MASKED, false>), grid, dim3(512), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if constexpr (MASKED) {
+    switch (key) {
+      case 64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 4, 2, true, true>), grid, dim3(256), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 4, 2, true, true>), grid, dim3(256), 0, stream, a); break;
+      case -64: hipLaunchKernelGGL((attn_bf16_vt_kernel<64, 8, 4, true, true>), grid, dim3(512), 0, stream, a); break;
+      case -128: hipLaunchKernelGGL((attn_bf16_vt_kernel<128, 8, 4, true, true>), grid, dim3(512), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit <= 1) return e;
