@@ -40,7 +40,10 @@ def parse():
     ap.add_argument("--workload", default="abot720")
     ap.add_argument("--fused-rope", action="store_true",
                     help="library-side rotation (raw q/k in, keys stored at absolute ids, no REL window pass); "
-                         "chunk_attention's time then includes its q/k rotation launches")
+                         "chunk_attention's time then includes its launch that rotates q/k and stages V")
+    ap.add_argument("--separate-prep", action="store_true",
+                    help="prepare each pass with rope_apply_qk + kv_cache_stage_v (two launches) instead of "
+                         "kv_cache_prepare_pass (one launch in bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--pool", type=int, default=2, help="device-resident input sets cycled over steps")
@@ -126,6 +129,7 @@ class Runner:
         self.chunk = 0
         self.ev = None
         self.kernel_events = True   # False: only the per-step event pair is recorded
+        self.separate_prep = False  # True: rope_apply_qk + stage_v instead of prepare_pass
 
     def prefill(self):
         si, wl, cfg = self.si, self.wl, self.cfg
@@ -160,17 +164,21 @@ class Runner:
             for li, cache in enumerate(self.caches):
                 t = cache.info().n_appended
                 if self.fused:
-                    self._ev("stage0")
-                    cache.stage_v(v)
                     self._ev("attn0")
-                    cache.chunk_attention(q, k, None, out=self.out)   # rotates q and k first
+                    cache.chunk_attention(q, k, v, out=self.out)   # rotates q and k, stages v first
                     self._ev("attn1")
-                else:
+                elif self.separate_prep:
                     self._ev("rope0")
                     cache.rope_apply_qk(q, k, q_out=self.qr, k_out=self.kr[li], start_frame=t)
                     self._ev("rope1")
                     self._ev("stage0")
                     cache.stage_v(v)
+                    self._ev("attn0")
+                    cache.chunk_attention(self.qr, self.kr[li], None, out=self.out)
+                    self._ev("attn1")
+                else:
+                    self._ev("prep0")
+                    cache.prepare_pass(q, k, v, q_out=self.qr, k_out=self.kr[li], start_frame=t)
                     self._ev("attn0")
                     cache.chunk_attention(self.qr, self.kr[li], None, out=self.out)
                     self._ev("attn1")
@@ -410,6 +418,7 @@ def main():
     cfg = wl.cfg
     torch.cuda.set_device(0)
     r = Runner(wl, max(1, args.pool))
+    r.separate_prep = args.separate_prep
     r.prefill()
     mem = None
     if args.rollout:
@@ -423,7 +432,7 @@ def main():
         for _ in range(args.warmup):
             r.step()
     torch.cuda.synchronize()
-    ev_kinds = ("step0", "step1", "win0", "win1", "rope0", "rope1", "stage0", "attn0", "attn1",
+    ev_kinds = ("step0", "step1", "win0", "win1", "rope0", "rope1", "stage0", "prep0", "attn0", "attn1",
                 "cross0", "cross1", "app0", "app1", "samp0", "samp1")
     r.ev = {k: [] for k in ev_kinds}
     r.kernel_events = False   # the timed steps: one event pair per step, nothing between kernels
@@ -457,6 +466,7 @@ def main():
     stage_ms, _ = avg_ms(ev, "stage0", "attn0")
     app_ms, _ = avg_ms(ev, "app0", "app1")
     rope_ms, _ = avg_ms(ev, "rope0", "rope1")
+    prep_ms, _ = avg_ms(ev, "prep0", "attn0")
     win_ms, _ = avg_ms(ev, "win0", "win1")
     cross_ms, _ = avg_ms(ev, "cross0", "cross1")
     samp_ms, _ = avg_ms(ev, "samp0", "samp1")
@@ -490,6 +500,9 @@ def main():
         "config": {"workload": wl.name, "heads": h, "head_dim": d, "tokens_per_frame": f, "chunk_frames": c,
                    "sink_frames": cfg.sink_frames, "window_frames": cfg.window_frames, "lq": lq, "lkv": lkv,
                    "rope": "relative" if r.rel else "absolute", "fused_rope": r.fused,
+                   "pass_preparation": ("in chunk_attention" if r.fused else
+                                        "rope_apply_qk + kv_cache_stage_v" if r.separate_prep else
+                                        "kv_cache_prepare_pass"),
                    "layers": wl.layers, "passes_per_chunk": wl.passes,
                    "text_tokens": wl.text_tokens},
         "roofline": roof,
@@ -498,15 +511,21 @@ def main():
         "cache_update": {"GB/s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1),
                          "frac_hbm": round(app_bytes / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "avg_us": round(app_ms * 1e3, 2), "bytes": app_bytes},
-        "stage_v": {"GB/s": round(2 * lq * h * d * elt / (stage_ms * 1e-3) / 1e9, 1), "avg_us": round(stage_ms * 1e3, 2)},
         "per_chunk_ms": {"mean": round(float(np.mean(steps_ms)), 4), "p50": round(float(np.median(steps_ms)), 4),
                          "p99": round(float(np.percentile(steps_ms, 99)), 4),
                          "instrumented_mean": round(float(np.mean(steps_ms_instr)), 4)},
     }
-    if not r.fused:
+    stage_bytes = 2 * lq * h * d * elt                        # V read, V^T written
+    if r.fused:
+        out["chunk_attention"]["note"] = ("fused rotation: includes the launch that rotates q / k and stages V "
+                                          "before the kernel")
+    elif r.separate_prep:
         out["rope_qk"] = {"GB/s": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1), "avg_us": round(rope_ms * 1e3, 2)}
+        out["stage_v"] = {"GB/s": round(stage_bytes / (stage_ms * 1e-3) / 1e9, 1), "avg_us": round(stage_ms * 1e3, 2)}
     else:
-        out["chunk_attention"]["note"] = "fused rotation: includes the q / k rotation launches before the kernel"
+        out["prepare_pass"] = {"GB/s": round((rope_bytes + stage_bytes) / (prep_ms * 1e-3) / 1e9, 1),
+                               "avg_us": round(prep_ms * 1e3, 2), "bytes": rope_bytes + stage_bytes,
+                               "note": "kv_cache_prepare_pass: q and k rotated, V staged, one launch"}
     if wl.timesteps:
         # per call: x_t, velocity and noise read, x0 and the re-noised latent written (last step: x0 only)
         ns = len(wl.timesteps)

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 3
+#define SKV_ABI_VERSION 4
 
 typedef enum {
   SKV_OK = 0,
@@ -166,6 +166,17 @@ skv_status rope_apply_window(skv_cache* cache, void* stream);
  * it is given v_cur; calling it separately lets a caller time or overlap it.
  * n_frames must equal c. */
 skv_status kv_cache_stage_v(skv_cache* cache, const void* v_cur, int32_t n_frames, void* stream);
+
+/* Everything an attention pass needs before chunk_attention, in one launch: the
+ * result of rope_apply_qk(q_in -> q_out, k_in -> k_out, n_frames, start_frame)
+ * followed by kv_cache_stage_v(v_cur) ([LB-src] 改造③ rotates q and k with one
+ * start_frame; [LB-fast] 3. KV 缓存 滚动窗口 feeds the chunk's own K/V to the
+ * window attention).  bf16 runs the rotary blocks and the staging blocks in one
+ * grid, fp32 as two launches.  n_frames must equal c; argument errors are those
+ * of the two calls.  v_cur must not overlap q_out or k_out.  Then call
+ * chunk_attention(q_out, k_out, NULL). */
+skv_status kv_cache_prepare_pass(skv_cache* cache, const void* q_in, void* q_out, const void* k_in, void* k_out,
+                                 const void* v_cur, int32_t n_frames, int64_t start_frame, void* stream);
 
 /* Chunk attention ([LB-fast] 3. KV 缓存 滚动窗口: attention over the window
  * slice; [ABot-stream] 机制二: block-causal, frames of a chunk see each other).

@@ -26,7 +26,7 @@ EXPORTED = (
     "kv_cache_destroy", "kv_cache_append_evict", "rope_apply", "rope_apply_window", "chunk_attention",
     "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v", "sampler_step",
     "chunk_attention_batch", "block_causal_workspace_bytes", "block_causal_attention",
-    "text_cache_bytes", "text_cache_prepare", "cross_attention_cached", "rope_apply_qk",
+    "text_cache_bytes", "text_cache_prepare", "cross_attention_cached", "rope_apply_qk", "kv_cache_prepare_pass",
 )
 
 
@@ -71,6 +71,7 @@ def _load() -> ctypes.CDLL:
         "kv_cache_append_evict": ([vp, vp, vp, i32, vp], st),
         "rope_apply": ([vp, vp, vp, i32, i64, vp], st),
         "rope_apply_qk": ([vp, vp, vp, vp, vp, i32, i64, vp], st),
+        "kv_cache_prepare_pass": ([vp, vp, vp, vp, vp, vp, i32, i64, vp], st),
         "rope_apply_window": ([vp, vp], st),
         "chunk_attention": ([vp, vp, vp, vp, i32, vp, vp], st),
         "cross_attention": ([vp, i32, vp, vp, i32, i32, i32, i32, vp, vp], st),
@@ -228,6 +229,20 @@ class KVCache:
         k_out = torch.empty_like(k) if k_out is None else self._tensor(k_out, n, "k_out")
         _check(lib.rope_apply_qk(self._h, _ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out), n, int(start_frame),
                                  _stream(stream)), "rope_apply_qk")
+        return q_out, k_out
+
+    def prepare_pass(self, q: torch.Tensor, k: torch.Tensor, v_cur: torch.Tensor,
+                     q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                     start_frame: int = 0, stream=None):
+        """rope_apply_qk and stage_v in one call (one launch in bf16); returns (q_out, k_out)."""
+        c = self.cfg.chunk_frames
+        self._tensor(q, c, "q")
+        self._tensor(k, c, "k")
+        self._tensor(v_cur, c, "v_cur")
+        q_out = torch.empty_like(q) if q_out is None else self._tensor(q_out, c, "q_out")
+        k_out = torch.empty_like(k) if k_out is None else self._tensor(k_out, c, "k_out")
+        _check(lib.kv_cache_prepare_pass(self._h, _ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out), _ptr(v_cur), c,
+                                         int(start_frame), _stream(stream)), "kv_cache_prepare_pass")
         return q_out, k_out
 
     def rope_apply_window(self, stream=None) -> None:

@@ -1,12 +1,12 @@
-// Cache update, logical gather and 3D rotary kernels (gfx950).
+// Frame copy (cache update of keys, logical gather), 3D rotary and pass
+// preparation kernels (gfx950).
 //
-// All three are HBM-bound streaming kernels.  Work is organised by token: a
+// All are HBM-bound streaming kernels.  Work is organised by token: a
 // block owns a few tokens and its threads sweep the H*D elements of each token
 // in 16-byte vectors, so every global access is a run of at least D*elt
 // contiguous bytes on both the read and the write side, and index math per
 // vector is a shift and a mask.
-#include "skv_device.hpp"
-#include "skv_kernels.hpp"
+#include "stream_bodies.hpp"
 
 namespace skv {
 
@@ -81,109 +81,14 @@ hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], int n_
 }
 
 // ---------------------------------------------------------------- 3D RoPE
-// [LB-src] 改造③ / [LB-causal] "Attention Sink" (start_frame offset) and
-// [ABot-stream] 机制三 (relative ids over the visible window): token (frame i,
-// row r, col w) turns pair k of the [time | height | width] part of head_dim by
-// position * omega_k.  A block owns a few tokens and a group of kRopeHeads heads:
-// each thread computes cos/sin for its 4 pairs once (angle reduced mod 2*pi in
-// fp64, then fp32 sincos) and applies them to every head of the group, issuing
-// all of its loads before the first store.
-constexpr int kRopeThreads = 256;
-constexpr int kRopeHeads = 8;
-
-struct RopeArgs {
-  RopeJob jobs[3];     // per grid z: tensors, time id of launch frame 0 (before clamping), clamp (>= 0)
-  FrameRun runs[3];
-  int32_t nruns;
-  int32_t F, gw, H, D;
-  int32_t pair_h, pair_w;  // first pair index of the height / width parts
-  int32_t n_tok;
-  double omega[64];    // per pair, theta^(-2k/d_axis) with k counted inside its axis
-};
-
-template <typename T>
-struct RopeIo;
-
-template <>
-struct RopeIo<__bf16> {
-  typedef u32x4_t V;  // 8 elements
-  static __device__ __forceinline__ V load(const __bf16* p) { return *(const V*)p; }
-  static __device__ __forceinline__ void rot_store(__bf16* d, const V& w, const float (&cs)[4], const float (&sn)[4]) {
-    u32x4_t o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float x0 = bf16_lo_to_f32(w[p]), x1 = bf16_hi_to_f32(w[p]);
-      o[p] = pack_bf16x2(x0 * cs[p] - x1 * sn[p], x0 * sn[p] + x1 * cs[p]);
-    }
-    *(u32x4_t*)d = o;
-  }
-};
-
-template <>
-struct RopeIo<float> {
-  struct V {
-    f32x4_t a, b;
-  };
-  static __device__ __forceinline__ V load(const float* p) { return V{*(const f32x4_t*)p, *(const f32x4_t*)(p + 4)}; }
-  static __device__ __forceinline__ void rot_store(float* d, const V& v, const float (&cs)[4], const float (&sn)[4]) {
-    const float x[8] = {v.a[0], v.a[1], v.a[2], v.a[3], v.b[0], v.b[1], v.b[2], v.b[3]};
-    float y[8];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      y[2 * p] = x[2 * p] * cs[p] - x[2 * p + 1] * sn[p];
-      y[2 * p + 1] = x[2 * p] * sn[p] + x[2 * p + 1] * cs[p];
-    }
-    *(f32x4_t*)d = f32x4_t{y[0], y[1], y[2], y[3]};
-    *(f32x4_t*)(d + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
-  }
-};
-
+// Body and argument block in stream_bodies.hpp.  grid = (token blocks, head groups, tensors).
 template <typename T>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeArgs a) {
-  using IO = RopeIo<T>;
-  const int G = a.D >> 3;                 // groups of 4 pairs (8 elements) per row
-  const int tpb = kRopeThreads / G;       // tokens per block
-  const int g = threadIdx.x % G, tl = threadIdx.x / G;
-  const int gt = blockIdx.x * tpb + tl;   // token index in the launch
-  if (gt >= a.n_tok) return;
-  const int h0 = blockIdx.y * kRopeHeads;
-  const int nh = a.H - h0 < kRopeHeads ? a.H - h0 : kRopeHeads;
-  const int fi = gt / a.F, tok = gt - fi * a.F;
-  int sf = 0, df = 0;
-  for (int r = 0; r < a.nruns; ++r) {
-    const FrameRun run = a.runs[r];
-    if (fi >= run.start && fi < run.start + run.count) {
-      sf = run.src0 + (fi - run.start);
-      df = run.dst0 + (fi - run.start);
-    }
-  }
-  const RopeJob& j = a.jobs[blockIdx.z];
-  const T* s = (const T*)j.src.base + (int64_t)(sf * a.F + tok) * j.src.tok_stride + g * 8 + h0 * j.src.head_stride;
-  T* d = (T*)j.dst.base + (int64_t)(df * a.F + tok) * j.dst.tok_stride + g * 8 + h0 * j.dst.head_stride;
-  typename IO::V x[kRopeHeads];
-#pragma unroll
-  for (int i = 0; i < kRopeHeads; ++i)
-    if (i < nh) x[i] = IO::load(s + i * j.src.head_stride);
-  int64_t t = j.t0 + fi;
-  if (j.clamp_max >= 0) t = t < 0 ? 0 : (t > j.clamp_max ? j.clamp_max : t);
-  const int row = tok / a.gw, col = tok - row * a.gw;
-  float cs[4], sn[4];
-  const double two_pi = 6.283185307179586476925287;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int pair = g * 4 + p;
-    const double pos = pair < a.pair_h ? (double)t : (pair < a.pair_w ? (double)row : (double)col);
-    const double ang = pos * a.omega[pair];
-    const double red = ang - two_pi * rint(ang / two_pi);  // |red| <= pi
-    sincosf((float)red, &sn[p], &cs[p]);
-  }
-#pragma unroll
-  for (int i = 0; i < kRopeHeads; ++i)
-    if (i < nh) IO::rot_store(d + i * j.dst.head_stride, x[i], cs, sn);
+  rope_block<T>(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
 }
 
-hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream) {
-  if (L.njobs < 1 || L.njobs > 3) return hipErrorInvalidValue;
+// Fills the argument block of a rotary launch and its grid.
+static RopeArgs rope_args(const RopeLaunch& L, dim3* grid) {
   RopeArgs a;
   for (int i = 0; i < 3; ++i) a.jobs[i] = L.job[i < L.njobs ? i : 0];
   for (int i = 0; i < 3; ++i) a.runs[i] = i < L.nruns ? L.runs[i] : FrameRun{0, 0, 0, 0};
@@ -203,11 +108,68 @@ hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream) {
   for (; p < 64; ++p) a.omega[p] = 0.0;
   const int G = L.D / 8;
   const int tpb = kRopeThreads / G;
-  dim3 grid((a.n_tok + tpb - 1) / tpb, (L.H + kRopeHeads - 1) / kRopeHeads, L.njobs);
+  *grid = dim3((a.n_tok + tpb - 1) / tpb, (L.H + kRopeHeads - 1) / kRopeHeads, L.njobs);
+  return a;
+}
+
+hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream) {
+  if (L.njobs < 1 || L.njobs > 3) return hipErrorInvalidValue;
+  dim3 grid;
+  const RopeArgs a = rope_args(L, &grid);
   if (L.dtype_bf16)
     hipLaunchKernelGGL(rope_kernel<__bf16>, grid, dim3(kRopeThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(kRopeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pass preparation
+// The rotary blocks of a launch (q, k_cur, ...) and the blocks staging the chunk's V^T, in one
+// bf16 grid: workgroups [0, n_rope) are rotary blocks in the rotary grid's order (x fastest),
+// the rest carry kRopeThreads / write_block_threads() staging blocks each.  The two kinds read
+// and write disjoint tensors, so their order within the grid does not matter; one launch saves
+// the gap and the ramp of a second one before the attention pass.
+template <int D>
+__global__ __launch_bounds__(kRopeThreads) void prepare_pass_kernel(RopeArgs r, WriteArgs w, int rope_gx,
+                                                                    int rope_gy, int n_rope, int stage_gx,
+                                                                    int n_stage) {
+  const int b = blockIdx.x;
+  if (b < n_rope) {
+    const int yz = b / rope_gx;
+    rope_block<__bf16>(r, b - yz * rope_gx, yz % rope_gy, yz / rope_gy, threadIdx.x);
+  } else {
+    constexpr int WT = write_block_threads<uint16_t, D>();
+    static_assert(kRopeThreads % WT == 0, "staging blocks must tile the workgroup");
+    const int sb = (b - n_rope) * (kRopeThreads / WT) + (int)threadIdx.x / WT;
+    if (sb >= n_stage) return;
+    write_kv_block<uint16_t, D>(w, sb % stage_gx, sb / stage_gx, (int)threadIdx.x % WT);
+  }
+}
+
+hipError_t launch_prepare_pass(const RopeLaunch& L, const WriteArgs& w, hipStream_t stream) {
+  if (L.njobs < 1 || L.njobs > 3 || !L.dtype_bf16 || w.nruns != 0 || L.D != w.D) return hipErrorInvalidValue;
+  dim3 rg;
+  const RopeArgs r = rope_args(L, &rg);
+  const int n_rope = (int)(rg.x * rg.y * rg.z);
+  const int stage_gx = (w.row_pad + kTT - 1) / kTT;
+  const int n_stage = stage_gx * w.H;
+  int per_wg;
+  switch (w.D) {
+    case 64: per_wg = kRopeThreads / write_block_threads<uint16_t, 64>(); break;
+    case 128: per_wg = kRopeThreads / write_block_threads<uint16_t, 128>(); break;
+    default: return hipErrorInvalidValue;
+  }
+  const dim3 grid(n_rope + (n_stage + per_wg - 1) / per_wg);
+  switch (w.D) {
+    case 64:
+      hipLaunchKernelGGL(prepare_pass_kernel<64>, grid, dim3(kRopeThreads), 0, stream, r, w, (int)rg.x, (int)rg.y,
+                         n_rope, stage_gx, n_stage);
+      break;
+    default:
+      hipLaunchKernelGGL(prepare_pass_kernel<128>, grid, dim3(kRopeThreads), 0, stream, r, w, (int)rg.x, (int)rg.y,
+                         n_rope, stage_gx, n_stage);
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -64,6 +64,8 @@ struct RopeLaunch {
   bool dtype_bf16;
 };
 hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream);
+// bf16, D in {64, 128}: the rotary launch L and the staging write w (nruns == 0) as one grid.
+hipError_t launch_prepare_pass(const RopeLaunch& L, const WriteArgs& w, hipStream_t stream);
 
 // softmax(q K^T * scale) V over the concatenated key ranges of a.seg.
 // bf16, V transposed (cache path) / V token-major (cross attention); fp32 takes any V strides.

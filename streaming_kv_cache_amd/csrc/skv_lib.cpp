@@ -91,7 +91,7 @@ void* ws_q_rel(const skv_cache* c) { return (char*)ws_k_cur(c) + chunk_elems(c->
 void* ws_vt(const skv_cache* c) { return (char*)c->ws + (ws_window_elems(c->g) + ws_fused_elems(c->g)) * c->g.elt; }
 
 // Current chunk's V -> V^T rows in the workspace (tail zero-filled to a multiple of 64 keys).
-skv_status stage_v(skv_cache* c, const void* v_cur, void* stream) {
+skv::WriteArgs stage_args(const skv_cache* c, const void* v_cur) {
   const skv::Geometry& g = c->g;
   skv::WriteArgs wa{};
   wa.k_src = nullptr;
@@ -107,7 +107,20 @@ skv_status stage_v(skv_cache* c, const void* v_cur, void* stream) {
   wa.D = g.D;
   wa.n_tok = g.c * g.F;
   wa.row_pad = (int32_t)cur_row(g);
-  return launched(c, skv::launch_write_kv(wa, g.elt, (hipStream_t)stream));
+  return wa;
+}
+
+skv_status stage_v(skv_cache* c, const void* v_cur, void* stream) {
+  return launched(c, skv::launch_write_kv(stage_args(c, v_cur), c->g.elt, (hipStream_t)stream));
+}
+
+// A rotary launch and the staging of v_cur: one grid in bf16, two launches in fp32.
+skv_status rope_and_stage(skv_cache* c, const skv::RopeLaunch& L, const void* v_cur, void* stream) {
+  const skv::WriteArgs w = stage_args(c, v_cur);
+  if (c->g.dtype == SKV_BF16) return launched(c, skv::launch_prepare_pass(L, w, (hipStream_t)stream));
+  const skv_status st = launched(c, skv::launch_rope(L, (hipStream_t)stream));
+  if (st != SKV_OK) return st;
+  return launched(c, skv::launch_write_kv(w, c->g.elt, (hipStream_t)stream));
 }
 
 // Rotary launch over n_frames frames of a token-major tensor (or the store, via runs).
@@ -134,7 +147,7 @@ skv::RopeLaunch rope_launch(const skv::Geometry& g, skv::TokView src, skv::TokVi
 
 // Fused rotation before an attention pass, into the workspace, in one launch: job 0 q at absolute
 // ids, job 1 k_cur at absolute ids, job 2 (REL with visible sinks) q at slot ids.
-skv_status fused_prepare(skv_cache* c, const void* q, const void* k_cur, void* stream) {
+skv::RopeLaunch fused_rope_launch(const skv_cache* c, const void* q, const void* k_cur) {
   const skv::Geometry& g = c->g;
   const skv::VisiblePlan p = c->ring.plan(g, g.c);
   const int64_t T = c->ring.T;
@@ -143,7 +156,7 @@ skv_status fused_prepare(skv_cache* c, const void* q, const void* k_cur, void* s
   L.njobs = 2;
   if (g.mode == SKV_ROPE_REL && p.n_sink_vis > 0)
     L.job[L.njobs++] = skv::RopeJob{token_view(g, q), token_view(g, ws_q_rel(c)), p.n_vis - g.c, g.W - 1};
-  return launched(c, skv::launch_rope(L, (hipStream_t)stream));
+  return L;
 }
 
 }  // namespace
@@ -284,10 +297,10 @@ skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int
   return SKV_OK;
 }
 
-// rope_apply / rope_apply_qk: one launch over n (1 or 2) tensors with the same time ids.
-static skv_status rope_tensors(const skv_cache* cc, const void* const* in, void* const* out, int n, int32_t n_frames,
-                               int64_t start_frame, void* stream) {
-  skv_cache* c = const_cast<skv_cache*>(cc);
+// rope_apply / rope_apply_qk / kv_cache_prepare_pass: checks n (1 or 2) tensors and describes one
+// rotary launch over them with the same time ids; enqueues nothing.
+static skv_status rope_plan(const skv_cache* c, const void* const* in, void* const* out, int n, int32_t n_frames,
+                            int64_t start_frame, skv::RopeLaunch* L) {
   skv_status st = check_handle(c);
   if (st != SKV_OK) return st;
   for (int i = 0; i < n; ++i) {
@@ -308,9 +321,18 @@ static skv_status rope_tensors(const skv_cache* cc, const void* const* in, void*
     t0 = p.n_vis - g.c;
     clamp_max = g.W - 1;
   }
-  skv::RopeLaunch L = rope_launch(g, token_view(g, in[0]), token_view(g, out[0]), n_frames, t0, clamp_max);
-  for (int i = 1; i < n; ++i) L.job[i] = skv::RopeJob{token_view(g, in[i]), token_view(g, out[i]), t0, clamp_max};
-  L.njobs = n;
+  *L = rope_launch(g, token_view(g, in[0]), token_view(g, out[0]), n_frames, t0, clamp_max);
+  for (int i = 1; i < n; ++i) L->job[i] = skv::RopeJob{token_view(g, in[i]), token_view(g, out[i]), t0, clamp_max};
+  L->njobs = n;
+  return SKV_OK;
+}
+
+static skv_status rope_tensors(const skv_cache* cc, const void* const* in, void* const* out, int n, int32_t n_frames,
+                               int64_t start_frame, void* stream) {
+  skv_cache* c = const_cast<skv_cache*>(cc);
+  skv::RopeLaunch L;
+  const skv_status st = rope_plan(c, in, out, n, n_frames, start_frame, &L);
+  if (st != SKV_OK) return st;
   return launched(c, skv::launch_rope(L, (hipStream_t)stream));
 }
 
@@ -326,6 +348,20 @@ skv_status rope_apply_qk(const skv_cache* cache, const void* q_in, void* q_out, 
   const void* in[2] = {q_in, k_in};
   void* out[2] = {q_out, k_out};
   return rope_tensors(cache, in, out, 2, n_frames, start_frame, stream);
+}
+
+skv_status kv_cache_prepare_pass(skv_cache* c, const void* q_in, void* q_out, const void* k_in, void* k_out,
+                                 const void* v_cur, int32_t n_frames, int64_t start_frame, void* stream) {
+  const void* in[2] = {q_in, k_in};
+  void* out[2] = {q_out, k_out};
+  skv::RopeLaunch L;
+  skv_status st = rope_plan(c, in, out, 2, n_frames, start_frame, &L);
+  if (st != SKV_OK) return st;
+  if ((st = check_ptr(v_cur)) != SKV_OK) return st;
+  if (n_frames != c->g.c) return SKV_ERR_SHAPE;
+  st = rope_and_stage(c, L, v_cur, stream);
+  if (st == SKV_OK) c->v_staged = true;
+  return st;
 }
 
 skv_status rope_apply_window(skv_cache* c, void* stream) {
@@ -364,7 +400,7 @@ static skv_status attention_args(skv_cache* c, const void* q, const void* k_cur,
   if (rel && !g.fused && p.n_hist > 0 && !c->window_ready) return SKV_ERR_STATE;
   if (!v_cur && !c->v_staged) return SKV_ERR_STATE;
 
-  // fused rotation: the workspace copies written by fused_prepare; REL sinks use the queries at
+  // fused rotation: the workspace copies written by the fused rotary launch; REL sinks use the queries at
   // slot ids, everything after them the queries at absolute ids
   a->q = q;
   a->q_alt = nullptr;
@@ -450,15 +486,16 @@ skv_status chunk_attention_batch(const skv_cache* const* caches, int32_t n_cache
   }
   // everything checked: rotate (fused), stage the values given, then one launch for all elements
   for (int i = 0; i < n_caches; ++i) {
+    const bool stage = v_cur && v_cur[i];
+    skv_status st = SKV_OK;
     if (cs[i]->g.fused) {
-      const skv_status st = fused_prepare(cs[i], q[i], k_cur[i], stream);
-      if (st != SKV_OK) return st;
+      const skv::RopeLaunch L = fused_rope_launch(cs[i], q[i], k_cur[i]);
+      st = stage ? rope_and_stage(cs[i], L, v_cur[i], stream) : launched(cs[i], skv::launch_rope(L, (hipStream_t)stream));
+    } else if (stage) {
+      st = stage_v(cs[i], v_cur[i], stream);
     }
-    if (v_cur && v_cur[i]) {
-      const skv_status st = stage_v(cs[i], v_cur[i], stream);
-      if (st != SKV_OK) return st;
-      cs[i]->v_staged = true;
-    }
+    if (st != SKV_OK) return st;
+    if (stage) cs[i]->v_staged = true;
   }
   const skv::Geometry& g = cs[0]->g;
   hipError_t e = hipSuccess;

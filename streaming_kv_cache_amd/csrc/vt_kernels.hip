@@ -1,119 +1,22 @@
-// Cache write-back and current-chunk staging: token-major [tokens, H, D] in,
-// head-major K rows and transposed V (V^T[h][d][key]) out (gfx950).
-//
-// A pure streaming kernel: each thread moves a P x P block (P = elements per 16
-// bytes) of one head: P consecutive tokens times one 16-byte chunk of head_dim.
-// It issues all of its loads first (K and V), writes the K pieces to their slot
-// rows, transposes the V block in registers and writes P pieces of V^T rows.
-// All accesses are 16 bytes wide; threads are ordered so that each store
-// instruction covers whole 128-byte runs of a V^T row.  No LDS.
+// Cache write-back and current-chunk staging (K rows + transposed V, body in
+// stream_bodies.hpp) and the V^T -> token-major gather (gfx950).
 // [LB-fast] "3. KV 缓存 滚动窗口" / [ABot-stream] 机制二 (clean write-back of the
 // chunk's K/V); the slot of each frame comes from the ring mapping on the host
 // (FrameRun.dst0 = slot).
-#include "skv_device.hpp"
-#include "skv_kernels.hpp"
+#include "stream_bodies.hpp"
 
 namespace skv {
 
 namespace {
 
-constexpr int kTT = 64;   // tokens per workgroup
 constexpr int kThreads = 256;  // threads of the gather kernel
-
-template <typename T>
-struct Per16 {
-  static constexpr int n = 16 / sizeof(T);
-};
-
-// Frame position in key space (slot) of launch frame fi.
-__device__ __forceinline__ int frame_dst(const WriteArgs& a, int fi) {
-  int df = fi;
-#pragma unroll
-  for (int r = 0; r < 3; ++r)
-    if (r < a.nruns && fi >= a.runs[r].start && fi < a.runs[r].start + a.runs[r].count)
-      df = a.runs[r].dst0 + (fi - a.runs[r].start);
-  return df;
-}
-
-// Element e of each of the P 16-byte rows in, gathered into one 16-byte row: the
-// transpose of a P x P block of 16- or 32-bit elements.
-template <typename T>
-__device__ __forceinline__ u32x4_t column(const u32x4_t (&in)[Per16<T>::n], int e) {
-  u32x4_t r;
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = (in[2 * w][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      const uint32_t hi = (in[2 * w + 1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      r[w] = lo | (hi << 16);
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) r[w] = in[w][e];
-  }
-  return r;
-}
 
 }  // namespace
 
-// grid = (ceil(n_tok / 64) [or row_pad / 64 for staging], H); block = (64 / P) * (D / P) threads.
-// Thread tid: token group tg = tid % (64 / P) (tokens t0 + P tg ...), chunk dc = tid / (64 / P).
+// grid = (ceil(n_tok / 64) [or row_pad / 64 for staging], H); block = write_block_threads<T, D>().
 template <typename T, int D>
-__global__ __launch_bounds__(kTT / Per16<T>::n * (D / Per16<T>::n)) void write_kv_kernel(WriteArgs a) {
-  constexpr int P = Per16<T>::n;  // elements per 16 bytes
-  constexpr int NG = kTT / P;     // token groups per workgroup
-  const int h = blockIdx.y;
-  const int tg = threadIdx.x % NG, dc = threadIdx.x / NG;
-  const int tb = blockIdx.x * kTT + tg * P;  // first token of this thread's block
-
-  u32x4_t kv[P], vv[P];
-  const u32x4_t z = {0u, 0u, 0u, 0u};
-  // ---- every load first
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const bool ok = tb + j < a.n_tok;
-    const int64_t off = (int64_t)(tb + j) * a.tok_stride + h * a.head_stride + dc * P;
-    kv[j] = (a.k_src && ok) ? *(const u32x4_t*)((const T*)a.k_src + off) : z;
-    vv[j] = ok ? *(const u32x4_t*)((const T*)a.v_src + off) : z;
-  }
-  // ---- K pieces -> head-major store rows (frame slot * F + token)
-  if (a.k_src) {
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int gt = tb + j;
-      if (gt < a.n_tok) {
-        const int fi = gt / a.F, tok = gt - fi * a.F;
-        const int64_t key = (int64_t)frame_dst(a, fi) * a.F + tok;
-        *(u32x4_t*)((T*)a.k_dst + h * a.k_hs + key * D + dc * P) = kv[j];
-      }
-    }
-  }
-  // ---- V: P rows of V^T (d = dc * P + e), keys tb .. tb + P - 1
-  T* vh = (T*)a.vt_dst + h * a.vt_hs;
-  if (a.nruns == 0) {
-    // staging: key = token; the row tail up to row_pad is written with the zeros loaded for it
-    if (tb < a.row_pad) {
-#pragma unroll
-      for (int e = 0; e < P; ++e) *(u32x4_t*)(vh + (int64_t)(dc * P + e) * a.vt_ds + tb) = column<T>(vv, e);
-    }
-  } else if (tb < a.n_tok) {
-    const int fi = tb / a.F, tok = tb - fi * a.F;
-    const int64_t k0 = (int64_t)frame_dst(a, fi) * a.F + tok;
-    const bool whole = tb + P <= a.n_tok && tok + P <= a.F && (k0 % P) == 0 && (a.vt_ds % P) == 0 &&
-                       ((uintptr_t)vh & 15) == 0;
-    if (whole) {
-#pragma unroll
-      for (int e = 0; e < P; ++e) *(u32x4_t*)(vh + (int64_t)(dc * P + e) * a.vt_ds + k0) = column<T>(vv, e);
-    } else {
-      for (int j = 0; j < P && tb + j < a.n_tok; ++j) {
-        const int gt = tb + j, f2 = gt / a.F;
-        const int64_t key = (int64_t)frame_dst(a, f2) * a.F + (gt - f2 * a.F);
-        const T* src = (const T*)&vv[j];
-#pragma unroll
-        for (int e = 0; e < P; ++e) vh[(int64_t)(dc * P + e) * a.vt_ds + key] = src[e];
-      }
-    }
-  }
+__global__ __launch_bounds__((write_block_threads<T, D>())) void write_kv_kernel(WriteArgs a) {
+  write_kv_block<T, D>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // V^T -> token-major (logical gather, not on the hot path).  grid = (ceil(n_tok / 64), H);

@@ -43,14 +43,20 @@ def fused(wl):
 
 def gpu_pass(cache, q, k, v):
     """rope(q), rope(k) at the chunk's ids, then chunk attention; returns (out, k to append, v).
-    With fused rotation the raw tensors go in as they are."""
+    With fused rotation the raw tensors go in as they are.  Chunks alternate between two call
+    sequences so that both meet the oracle: rope_apply twice then chunk_attention with v, and
+    kv_cache_prepare_pass (one launch) then chunk_attention over the staged values."""
     t = cache.info().n_appended
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     if cache.cfg.fused_rope:
         return cache.chunk_attention(qd, kd, vd), kd, vd
-    qr = cache.rope_apply(qd, start_frame=t)
-    kr = cache.rope_apply(kd, start_frame=t)
-    out = cache.chunk_attention(qr, kr, vd)
+    if (t // cache.cfg.chunk_frames) % 2 == 1:
+        qr, kr = cache.prepare_pass(qd, kd, vd, start_frame=t)
+        out = cache.chunk_attention(qr, kr, None)
+    else:
+        qr = cache.rope_apply(qd, start_frame=t)
+        kr = cache.rope_apply(kd, start_frame=t)
+        out = cache.chunk_attention(qr, kr, vd)
     k_store = kr if cache.cfg.rope_mode == skv.ROPE_ABS else kd
     return out, k_store, vd
 

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert skv.lib.skv_abi_version() == 3
+    assert skv.lib.skv_abi_version() == 4
     for code in range(7):
         assert skv.status_string(code)
     assert skv.status_string(99) == "unknown status"
@@ -121,9 +121,17 @@ def test_init_validation_and_info():
     assert qk(h, p, p, p, nul, 4, 0, nul) == skv.ERR_NULL
     assert qk(h, p, ctypes.c_void_p(0x40008), p, p, 4, 0, nul) == skv.ERR_ALIGN
     assert qk(h, p, p, p, p, 0, 0, nul) == skv.ERR_SHAPE
+    pp = skv.lib.kv_cache_prepare_pass  # rope_apply_qk's checks, then v_cur's, and n_frames == c
+    assert pp(h, p, p, p, p, p, 4, -1, nul) == skv.ERR_SHAPE
+    assert pp(h, p, p, nul, p, p, 4, 0, nul) == skv.ERR_NULL
+    assert pp(h, p, p, p, p, nul, 4, 0, nul) == skv.ERR_NULL
+    assert pp(h, p, p, p, p, ctypes.c_void_p(0x40008), 4, 0, nul) == skv.ERR_ALIGN
+    assert pp(h, p, p, p, p, p, 3, 0, nul) == skv.ERR_SHAPE                   # abs too: staging needs c frames
+    assert pp(nul, p, p, p, p, p, 4, 0, nul) == skv.ERR_NULL
     skv.lib.kv_cache_destroy(h)
     st, h = _init(ABOT)
     assert skv.lib.rope_apply_qk(h, p, p, p, p, 2, 0, nul) == skv.ERR_SHAPE   # rel: n_frames must equal c
+    assert skv.lib.kv_cache_prepare_pass(h, p, p, p, p, p, 2, 0, nul) == skv.ERR_SHAPE
     skv.lib.kv_cache_destroy(h)
 
 

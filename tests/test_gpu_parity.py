@@ -132,6 +132,34 @@ def test_rope_apply_qk_matches_two_calls(name):
     assert torch.equal(q2, rq) and torch.equal(k2, rk)
 
 
+@pytest.mark.parametrize("name", ["tiny", "small_abs", "small_rel", "small_d64", "small_f32_rel", "lb480", "abot720"])
+def test_prepare_pass_matches_separate_calls(name):
+    """kv_cache_prepare_pass (rotary and V^T staging blocks in one grid for bf16) writes exactly the bytes
+    of rope_apply_qk followed by kv_cache_stage_v: the rotated q and k compare bitwise, and attention over
+    the values it staged equals, bitwise, attention that stages the same values itself."""
+    wl = WORKLOADS[name]
+    c = wl.cfg
+    say(f"[prepare pass] {name}")
+    cache = skv.KVCache(c)
+    ro.prefill(wl, cache, None)
+    for ch in range(3):
+        cache.append_evict(ro.draw(wl, c.chunk_frames, ch, 4, si.K).cuda(), ro.draw(wl, c.chunk_frames, ch, 4, si.V).cuda())
+    if c.rope_mode == skv.ROPE_REL:
+        cache.rope_apply_window()
+    start = cache.info().n_appended
+    q = ro.draw(wl, c.chunk_frames, 5, 0, si.Q).cuda()
+    k = ro.draw(wl, c.chunk_frames, 5, 0, si.K).cuda()
+    v = ro.draw(wl, c.chunk_frames, 5, 0, si.V).cuda()
+    rq, rk = cache.rope_apply_qk(q, k, start_frame=start)
+    ref = cache.chunk_attention(rq, rk, v)
+    cache.stage_v(ro.draw(wl, c.chunk_frames, 6, 0, si.V).cuda())  # other values in the staging area first
+    gq, gk = cache.prepare_pass(q, k, v, start_frame=start)
+    got = cache.chunk_attention(gq, gk, None)
+    torch.cuda.synchronize()
+    assert torch.equal(gq, rq) and torch.equal(gk, rk)
+    assert torch.equal(got, ref)
+
+
 @pytest.mark.parametrize("name", ["small_rel", "small_f32_rel", "abot720"])
 def test_rope_rel_and_window(name):
     wl = WORKLOADS[name]
