@@ -63,7 +63,7 @@ def parse():
 
 
 def box_peak(torch):
-    """Dense bf16 peak from what the box reports: CUs x 4096 flop per clock x the peak engine clock
+    """Dense bf16 peak from what the device reports: CUs x 4096 flop per clock x the peak engine clock
     (hipDeviceAttributeClockRate, kHz).  None where the runtime does not answer."""
     import ctypes
     try:
@@ -405,7 +405,7 @@ def traffic_from_profile(wl_name, per_launch_algo_bytes):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build targets one GPU: run with --gpus 1 (no multi-GPU path)"}))
+        print(json.dumps({"error": "runs on one GPU: use --gpus 1 (no multi-GPU path)"}))
         sys.exit(2)
     sys.path.insert(0, ROOT)
     import torch
