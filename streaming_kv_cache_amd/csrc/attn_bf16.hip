@@ -771,16 +771,33 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 
     if (t == alt_tiles) load_q(a.q_alt);
     const uint8_t* kt = smem + st * KT_B;
-    // ---- keys 0..31: S'^T = K (Q^T * scale * log2 e)
-    // all LDS reads of a product are issued before its first MFMA (sched_barrier keeps them there)
-    bf16x8_t ka[KSTEPS];
+    const uint8_t* vt = smem + NSTAGE * KT_B + st * VT_B;
+    // One rolling set of A-operand registers: the LDS reads of the next product group are issued
+    // one after each product of the current group, into the slots it has just consumed, so they
+    // land while the matrix core works instead of stalling the next group's first product (and the
+    // exponentials behind it).  K of keys 32..63 rolls behind the first score products in both
+    // shapes; V rolls behind the preceding products only in the 8-wave shape, where it was
+    // measured faster (the 4-wave shape, two workgroups per CU, ran slower with it).
+    constexpr bool RV = NW == 8;
+    static_assert(KSTEPS == 2 * MBLK, "K steps and V blocks share the operand slots");
+    bf16x8_t ob[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = ld_bf16x8(kt + koff[0] + 32 * ks);
+    for (int ks = 0; ks < KSTEPS; ++ks) ob[ks] = ld_bf16x8(kt + koff[0] + 32 * ks);
     __builtin_amdgcn_sched_barrier(0);
+    // ---- keys 0..31: S'^T = K (Q^T * scale * log2 e); K of keys 32..63 read behind the products
     f32x16_t s0 = negm;
     if constexpr (FOLLOW) s0 = f32x16_t{};
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s0, 0, 0, 0);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[ks], qreg[ks], s0, 0, 0, 0);
+      ob[ks] = ld_bf16x8(kt + koff[1] + 32 * ks);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float sub0 = 0.f;
     if constexpr (MASKED) mask_half(s0, k0, nk);
     if constexpr (FOLLOW) {
@@ -805,19 +822,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       sub0 = 0.f;
     }
 
-    // ---- keys 32..63 on the matrix cores while P of keys 0..31 is formed
+    // ---- keys 32..63 on the matrix cores while P of keys 0..31 is formed (8 waves: and V of
+    // keys 0..31 is read)
     f32x16_t s1 = negm;
     if constexpr (FOLLOW) s1 = f32x16_t{};
     bf16x8_t pb[4];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = ld_bf16x8(kt + koff[1] + 32 * ks);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s1, 0, 0, 0);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[ks], qreg[ks], s1, 0, 0, 0);
+      if constexpr (RV) ob[ks] = ld_bf16x8(vt + voff + (ks % MBLK) * 32 * VP + 32 * (ks / MBLK));
+    }
     float lsum = exp_half(s0, sub0, pb[0], pb[1]);
 #pragma unroll
     for (int i = 0; i < KSTEPS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (RV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 48 / KSTEPS, 0);
     }
     // The running max is raised only when some score exceeds it by a lot (a row sum past
@@ -845,26 +864,37 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
         if (score_key(r, 0) >= nkh) s1[r] = -INFINITY;
     }
 
-    // ---- O^T += V^T P^T over keys 0..31 while P of keys 32..63 is formed
-    const uint8_t* vt = smem + NSTAGE * KT_B + st * VT_B;
-    bf16x8_t va[2 * MBLK];
+    // ---- O^T += V^T P^T over keys 0..31 while P of keys 32..63 is formed (8 waves: and V of
+    // keys 32..63 is read)
+    if constexpr (!RV) {
+#pragma unroll
+      for (int stp = 0; stp < 2; ++stp)
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) ob[stp * MBLK + mb] = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int stp = 0; stp < 2; ++stp)
 #pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb) va[stp * MBLK + mb] = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int stp = 0; stp < 2; ++stp)
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[stp * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
+      for (int mb = 0; mb < MBLK; ++mb) {
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[stp * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
+        if constexpr (RV) ob[stp * MBLK + mb] = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * (stp + 2));
+      }
     if constexpr (FOLLOW) {
       lsum = exp_half(s1, follow_max(s1), pb[2], pb[3]);
+      if constexpr (RV) {
+#pragma unroll
+        for (int i = 0; i < 2 * MBLK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
     } else {
       lsum = exp_half(s1, 0.f, pb[2], pb[3]);
 #pragma unroll
       for (int i = 0; i < 2 * MBLK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (RV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * MBLK), 0);
       }
       if (__any(lsum > 0x1p60f)) {
@@ -880,16 +910,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     }
     l_run += lsum;
     // ---- O^T += V^T P^T over keys 32..63
+    if constexpr (!RV) {
 #pragma unroll
-    for (int stp = 2; stp < 4; ++stp)
+      for (int stp = 2; stp < 4; ++stp)
 #pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb) va[(stp - 2) * MBLK + mb] = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int mb = 0; mb < MBLK; ++mb) ob[(stp - 2) * MBLK + mb] = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int stp = 2; stp < 4; ++stp)
 #pragma unroll
       for (int mb = 0; mb < MBLK; ++mb)
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[(stp - 2) * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[(stp - 2) * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
   }
 
   const float l_row = half_swap_sum(l_run);
