@@ -744,24 +744,50 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     }
   };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int st = t % NSTAGE;
-    const bool more = t + 1 < n_tiles;
-    // tile t landed (later tiles may still be in flight), then everyone is done with tile t-1,
-    // whose stage takes tile t + NSTAGE - 1
+  // Scheduling of the LDS operand reads.  All shapes keep the A operands in one rolling set of
+  // registers and read K of keys 32..63 behind the first score products.  The 8-wave shape also
+  // reads V behind the preceding products, and moves the tile's barrier from the top of the tile
+  // to before its last product group, so that K of the next tile's keys 0..31 is read behind that
+  // group too.  Each was measured faster for the 8-wave shape and slower for the 4-wave one (two
+  // workgroups per CU, whose waves already cover each other's waits).
+  constexpr bool ROLL_ALL = NW == 8;
+  static_assert(KSTEPS == 2 * MBLK, "K steps and V blocks share the operand slots");
+  bf16x8_t ob[KSTEPS];
+  if constexpr (ROLL_ALL) {
+    // tile 0 landed (later tiles may still be in flight), then K of its keys 0..31
     if constexpr (NSTAGE == 2)
       wait_vm_barrier<0>();
-    else if (t + 2 < n_tiles)
+    else if (n_tiles > 2)
       wait_vm_barrier<2 * (KMIN + VMIN)>();
-    else if (more)
+    else if (n_tiles > 1)
       wait_vm_barrier<KMIN + VMIN>();
     else
       wait_vm_barrier<0>();
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) ob[ks] = ld_bf16x8(smem + koff[0] + 32 * ks);
+  }
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int st = t % NSTAGE;
+    const bool more = t + 1 < n_tiles;
+    if constexpr (!ROLL_ALL) {
+      // tile t landed (later tiles may still be in flight), then everyone is done with tile t-1
+      if constexpr (NSTAGE == 2)
+        wait_vm_barrier<0>();
+      else if (t + 2 < n_tiles)
+        wait_vm_barrier<2 * (KMIN + VMIN)>();
+      else if (more)
+        wait_vm_barrier<KMIN + VMIN>();
+      else
+        wait_vm_barrier<0>();
+    }
     const int nk = nkq[0], k0 = k0q[0];
     nkq[0] = nkq[1];
     nkq[1] = nkq[2];
     k0q[0] = k0q[1];
     k0q[1] = k0q[2];
+    // the stage of tile t-1, which every wave is done with (behind the last barrier), takes
+    // tile t + NSTAGE - 1
     if (t + NSTAGE - 1 < n_tiles) {
       const int sn = (t + NSTAGE - 1) % NSTAGE;
       nkq[NSTAGE - 2] = issue_k(sn);
@@ -772,17 +798,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     if (t == alt_tiles) load_q(a.q_alt);
     const uint8_t* kt = smem + st * KT_B;
     const uint8_t* vt = smem + NSTAGE * KT_B + st * VT_B;
-    // One rolling set of A-operand registers: the LDS reads of the next product group are issued
-    // one after each product of the current group, into the slots it has just consumed, so they
-    // land while the matrix core works instead of stalling the next group's first product (and the
-    // exponentials behind it).  K of keys 32..63 rolls behind the first score products in both
-    // shapes; V rolls behind the preceding products only in the 8-wave shape, where it was
-    // measured faster (the 4-wave shape, two workgroups per CU, ran slower with it).
-    constexpr bool RV = NW == 8;
-    static_assert(KSTEPS == 2 * MBLK, "K steps and V blocks share the operand slots");
-    bf16x8_t ob[KSTEPS];
+    // The LDS reads of the next product group are issued one after each product of the current
+    // group, into the operand slots it has just consumed, so they land while the matrix core works
+    // instead of stalling the next group's first product (and the exponentials queued behind it).
+    constexpr bool RV = ROLL_ALL;
+    if constexpr (!ROLL_ALL) {
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) ob[ks] = ld_bf16x8(kt + koff[0] + 32 * ks);
+      for (int ks = 0; ks < KSTEPS; ++ks) ob[ks] = ld_bf16x8(kt + koff[0] + 32 * ks);
+    }
     __builtin_amdgcn_sched_barrier(0);
     // ---- keys 0..31: S'^T = K (Q^T * scale * log2 e); K of keys 32..63 read behind the products
     f32x16_t s0 = negm;
@@ -909,7 +932,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       }
     }
     l_run += lsum;
-    // ---- O^T += V^T P^T over keys 32..63
     if constexpr (!RV) {
 #pragma unroll
       for (int stp = 2; stp < 4; ++stp)
@@ -917,11 +939,44 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
         for (int mb = 0; mb < MBLK; ++mb) ob[(stp - 2) * MBLK + mb] = ld_bf16x8(vt + voff + mb * 32 * VP + 32 * stp);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (ROLL_ALL) {
+      // tile t+1 landed, and every wave holds all it reads of tile t (the wait includes the LDS
+      // reads), so tile t's stage is free from here on
+      if (more) {
+        if constexpr (NSTAGE == 2)
+          wait_vm_barrier<0>();
+        else if (t + 3 < n_tiles)
+          wait_vm_barrier<2 * (KMIN + VMIN)>();
+        else if (t + 2 < n_tiles)
+          wait_vm_barrier<KMIN + VMIN>();
+        else
+          wait_vm_barrier<0>();
+      }
+      // ---- O^T += V^T P^T over keys 32..63, K of keys 0..31 of tile t+1 read behind the products
+      // (after the last tile: a read of a stage nobody writes any more, never used)
+      const uint8_t* kn = smem + ((t + 1) % NSTAGE) * KT_B;
 #pragma unroll
-    for (int stp = 2; stp < 4; ++stp)
+      for (int stp = 2; stp < 4; ++stp)
 #pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[(stp - 2) * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
+        for (int mb = 0; mb < MBLK; ++mb) {
+          const int i = (stp - 2) * MBLK + mb;
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[i], pb[stp], o[mb], 0, 0, 0);
+          ob[i] = ld_bf16x8(kn + koff[0] + 32 * i);
+        }
+#pragma unroll
+      for (int i = 0; i < 2 * MBLK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // ---- O^T += V^T P^T over keys 32..63
+#pragma unroll
+      for (int stp = 2; stp < 4; ++stp)
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[(stp - 2) * MBLK + mb], pb[stp], o[mb], 0, 0, 0);
+    }
   }
 
   const float l_row = half_swap_sum(l_run);
