@@ -222,11 +222,20 @@ def cpu_baseline(runner, target_s):
     """Time the oracle (as it stands) on a bounded sample of one steady pass: a subset of query rows."""
     import seeded_inputs as si
     from oracle import skv_oracle as so
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info if i.get("user_api") == "blas"}))
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
     wl, cfg = runner.wl, runner.cfg
     orc = so.StreamingOracle(cfg.heads, cfg.head_dim, cfg.grid_h, cfg.grid_w, cfg.chunk_frames, cfg.sink_frames,
                              cfg.window_frames, rope_mode="rel" if runner.rel else "abs")
@@ -263,6 +272,7 @@ def cpu_baseline(runner, target_s):
     dt = total / reps
     flops = 4.0 * len(rows) * lkv * cfg.head_dim * cfg.heads
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model, "host_cpus": len(os.sched_getaffinity(0)), "blas": blas,
             "sample": f"one steady {wl.name} pass (Lkv={lkv}), {len(rows)} of {lq} query rows x {cfg.heads} heads, "
                       f"fp64 NumPy incl. RoPE of the visible keys; {reps} call(s), {total:.1f} s"}
 
