@@ -5,7 +5,8 @@ absolute-RoPE handle of the same configuration), so the masked attention over th
 sequence is what streaming the chunks through a cache computes (the oracle's pin).  Small
 shapes cover: frames whose token count is not a multiple of 8 (unaligned V^T ranges), a
 context prefix before the first query frame, no sinks, query chunks inside the sink range,
-both kernel shapes; a 480P-sized sequence is checked on sampled rows.
+both kernel shapes; a 480P-sized sequence and an ABot 720P-sized one (5 context frames, then 22
+chunks of 3) are checked on sampled rows.
 """
 import numpy as np
 import pytest
@@ -91,3 +92,17 @@ def test_block_causal_480p_sampled():
     say(f"[block-causal] 480P n_frames={n} rows={len(rows)}")
     got, ref = _run("lb480", h, d, gh, gw, c, s, w, n, 0, rows=rows)
     ro.assert_close(got, ref, skv.BF16, "480P sampled rows")
+
+
+def test_block_causal_abot720_sampled():
+    """The ABot 720P shape the bench's many-chunk leg times: 24 heads, 5 context frames (the sinks)
+    then 22 chunks of 3 frames, window 21: sampled rows from the first chunk, the chunk where the
+    window starts sliding and the last chunk."""
+    h, d, gh, gw, c, s, w = 24, 128, 22, 40, 3, 5, 21
+    q0, n = 5, 5 + 22 * 3
+    f = gh * gw
+    rows = np.concatenate([np.arange(0, 3 * f, 97), np.arange(15 * f, 18 * f, 151),
+                           np.arange((n - q0 - 3) * f, (n - q0) * f, 89)])
+    say(f"[block-causal] ABot 720P n_frames={n} q_frame0={q0} rows={len(rows)}")
+    got, ref = _run("abot720", h, d, gh, gw, c, s, w, n, q0, rows=rows)
+    ro.assert_close(got, ref, skv.BF16, "ABot 720P sampled rows")
