@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -81,8 +82,13 @@ def box_peak(torch):
 
 
 def kernel_sha(name: str) -> str:
+    """Hash of a kernel source with its comments and whitespace removed: counters taken on the code
+    stay valid across comment edits, and any change to the code itself invalidates them."""
     p = os.path.join(ROOT, "streaming_kv_cache_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    src = open(p, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()[:16]
 
 
 class Runner:

@@ -7,7 +7,7 @@
 // chunk, so no mask is needed inside a range).  Tiles never cross a range, so
 // only the last tile of each range is partial.
 //
-// Two kernels:
+// Three kernels:
 //   * attn_bf16_vt_kernel (the cache path): V arrives transposed (V^T[h][d][key],
 //     the layout the V store keeps); K rows and V^T tiles go global -> LDS with
 //     direct-to-LDS buffer loads into padded, conflict-free layouts.  Two shapes:
@@ -35,6 +35,11 @@
 //     running max that is raised only when a row sum would pass 2^60 (the result
 //     is the same for any max); each 64-key tile is done in two 32-key halves so
 //     the exponentials of one half overlap the matrix products of the other;
+//   * the A operands (K rows, V^T rows) sit in one rolling set of registers: the LDS
+//     reads of the next product group are issued one behind each product of the
+//     current group, so they land under the matrix core (the 8-wave shape also
+//     moves its tile barrier before the last product group, so the next tile's
+//     first K reads roll behind it too);
 //   * deterministic: no atomics, fixed reduction order.
 #include <cstdlib>
 
