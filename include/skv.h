@@ -173,8 +173,9 @@ skv_status kv_cache_stage_v(skv_cache* cache, const void* v_cur, int32_t n_frame
  * start_frame; [LB-fast] 3. KV 缓存 滚动窗口 feeds the chunk's own K/V to the
  * window attention).  bf16 runs the rotary blocks and the staging blocks in one
  * grid, fp32 as two launches.  n_frames must equal c; argument errors are those
- * of the two calls.  v_cur must not overlap q_out or k_out.  Then call
- * chunk_attention(q_out, k_out, NULL). */
+ * of the two calls, and SKV_ERR_STATE under fused rotation (chunk_attention then
+ * rotates q and k_cur and stages v_cur itself, in one launch).  v_cur must not
+ * overlap q_out or k_out.  Then call chunk_attention(q_out, k_out, NULL). */
 skv_status kv_cache_prepare_pass(skv_cache* cache, const void* q_in, void* q_out, const void* k_in, void* k_out,
                                  const void* v_cur, int32_t n_frames, int64_t start_frame, void* stream);
 

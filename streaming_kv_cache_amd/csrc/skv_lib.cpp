@@ -359,6 +359,7 @@ skv_status kv_cache_prepare_pass(skv_cache* c, const void* q_in, void* q_out, co
   if (st != SKV_OK) return st;
   if ((st = check_ptr(v_cur)) != SKV_OK) return st;
   if (n_frames != c->g.c) return SKV_ERR_SHAPE;
+  if (c->g.fused) return SKV_ERR_STATE;  // chunk_attention rotates (and stages) itself
   st = rope_and_stage(c, L, v_cur, stream);
   if (st == SKV_OK) c->v_staged = true;
   return st;

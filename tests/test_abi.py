@@ -255,7 +255,7 @@ def test_block_causal_validation():
 
 def test_fused_rope_config():
     """fused_rope: 0/1 only; the workspace holds the rotated chunk copies instead of the REL window;
-    the window call is not used."""
+    the window call and the separate pass preparation are not used."""
     import dataclasses
     bad = dataclasses.replace(ABOT, fused_rope=True).c_struct()
     bad.fused_rope = 2
@@ -269,4 +269,7 @@ def test_fused_rope_config():
     st, h = _init(dataclasses.replace(ABOT, fused_rope=True))
     assert st == skv.OK
     assert skv.lib.rope_apply_window(h, ctypes.c_void_p(0)) == skv.ERR_STATE
+    p = ctypes.c_void_p(0x40000)
+    # chunk_attention rotates and stages by itself under fused rotation
+    assert skv.lib.kv_cache_prepare_pass(h, p, p, p, p, p, 3, 0, ctypes.c_void_p(0)) == skv.ERR_STATE
     skv.lib.kv_cache_destroy(h)
