@@ -1020,6 +1020,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
 // Split keys: merge the partial results of nsplit key ranges into out (bf16).  Thread i handles
 // row r = i / (D / 4) of the [Lq * H] rows and its dims 4 (i % (D / 4)) .. +3:
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s (empty splits: m = -inf).
+// One thread per (row, 4 consecutive d): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
+// splits in a fixed order.  The split loop is unrolled to the most splits the workspace holds, so
+// every partial load of a thread is in flight at once (the pass is short and latency-bound).
+constexpr int kMaxSplit = 16;
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* part_o, const float* part_ml, int nsplit,
                                                          int64_t rows, int D, uint16_t* out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1027,17 +1031,30 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* part_o, co
   if (i >= rows * q4) return;
   const int64_t r = i / q4;
   const int d = 4 * (int)(i - r * q4);
+  float m[kMaxSplit], l[kMaxSplit];
+  f32x4_t o[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s < nsplit) {
+      const f32x2_t ml = *(const f32x2_t*)(part_ml + 2 * (s * rows + r));
+      m[s] = ml[0];
+      l[s] = ml[1];
+      o[s] = *(const f32x4_t*)(part_o + (s * rows + r) * D + d);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[2 * (s * rows + r)]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < nsplit) M = fmaxf(M, m[s]);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float m = part_ml[2 * (s * rows + r)];
-    if (m == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(m - M);
-    L += w * part_ml[2 * (s * rows + r) + 1];
-    const f32x4_t o = *(const f32x4_t*)(part_o + (s * rows + r) * D + d);
-    acc += w * o;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s < nsplit && m[s] != -INFINITY) {
+      const float w = __builtin_amdgcn_exp2f(m[s] - M);
+      L += w * l[s];
+      acc += w * o[s];
+    }
   }
   const float inv = 1.f / L;
   *(u32x2_t*)(out + r * D + d) = u32x2_t{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
@@ -1066,7 +1083,7 @@ static hipError_t launch_vt(const AttnBatch& in, int D, hipStream_t stream) {
   if (!MASKED) {
     const char* se = std::getenv("SKV_ATTN_SPLIT");
     const int mode = (se && *se) ? std::atoi(se) : -1;
-    int cap = 1 << 30, max_tiles = 0;
+    int cap = kMaxSplit, max_tiles = 0;  // the merge pass handles at most kMaxSplit partials per row
     for (int i = 0; i < a.nb; ++i) {
       cap = a.b[i].split_cap < cap ? a.b[i].split_cap : cap;
       int nt = 0;
