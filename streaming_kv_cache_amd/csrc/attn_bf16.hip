@@ -813,6 +813,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- keys 0..31: S'^T = K (Q^T * scale * log2 e); K of keys 32..63 read behind the products
+    // 4-wave shape: the first score products (products and LDS reads only) issue at raised wave
+    // priority, so the wave of the other workgroup on the SIMD yields the issue slots to them
+    // (measured 0.75 % faster at ABot; no measurable effect in the 8-wave shape)
+    if constexpr (NW == 4) __builtin_amdgcn_s_setprio(2);
     f32x16_t s0 = negm;
     if constexpr (FOLLOW) s0 = f32x16_t{};
 #pragma unroll
@@ -826,6 +830,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NW == 4) __builtin_amdgcn_s_setprio(0);
     float sub0 = 0.f;
     if constexpr (MASKED) mask_half(s0, k0, nk);
     if constexpr (FOLLOW) {
