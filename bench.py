@@ -6,6 +6,9 @@ A step is one generated chunk in steady state (the cache window is full):
   when the workload has text tokens), the sampler step between denoise passes, and
   after the write-back pass kv_cache_append_evict.
 Inputs are seeded N(0,1) tensors already resident in HBM when timing starts.
+The default workload is the largest single-GPU configuration: 40 layers of the
+LingBot-like 480P layer with cross attention over 512 cached text tokens
+(`--workload` selects another: abot720, lb480, lb720, ...).
 
 Prints ONE JSON line.  `value` is whole-step attention throughput: the
 attention FLOPs of a step (4 * Lq * Lkv * D * H per pass, visible pairs only)
@@ -38,7 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="abot720")
+    # default: the largest single-GPU configuration (40 layers of the 480P layer, 512 cached text tokens)
+    ap.add_argument("--workload", default="fulldepth480")
     ap.add_argument("--fused-rope", action="store_true",
                     help="library-side rotation (raw q/k in, keys stored at absolute ids, no REL window pass); "
                          "chunk_attention's time then includes its launch that rotates q/k and stages V")
@@ -82,13 +86,17 @@ def box_peak(torch):
 
 
 def kernel_sha(name: str) -> str:
-    """Hash of a kernel source with its comments and whitespace removed: counters taken on the code
-    stay valid across comment edits, and any change to the code itself invalidates them."""
-    p = os.path.join(ROOT, "streaming_kv_cache_amd", "csrc", name)
-    src = open(p, encoding="utf-8").read()
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", " ", src)
-    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()[:16]
+    """Hash of a kernel source and of the library headers it includes, each with its comments and
+    whitespace removed: counters taken on the code stay valid across comment edits, and any change to
+    the code the kernel is compiled from invalidates them."""
+    csrc = os.path.join(ROOT, "streaming_kv_cache_amd", "csrc")
+    h = hashlib.sha256()
+    for part in (name, "skv_device.hpp", "skv_kernels.hpp"):
+        src = open(os.path.join(csrc, part), encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()[:16]
 
 
 class Runner:
@@ -225,7 +233,10 @@ def avg_ms(ev, a, b):
 
 
 def cpu_baseline(runner, target_s):
-    """Time the oracle (as it stands) on a bounded sample of one steady pass: a subset of query rows."""
+    """Time the oracle (as it stands) on a bounded sample of one steady layer-pass: a subset of query
+    rows through self attention over the visible window and, when the workload has text tokens,
+    cross attention over them.  For several layers and passes per chunk, the per-chunk oracle time is
+    extrapolated from that one layer-pass (x layers x passes) and stated as such."""
     import seeded_inputs as si
     from oracle import skv_oracle as so
     blas = None
@@ -257,14 +268,25 @@ def cpu_baseline(runner, target_s):
         orc.append(si.to_f64(k), si.to_f64(v))
         ch += 1
     q, k, v = [si.to_f64(x) for x in sets[0][0]]
+    text = None
+    if wl.text_tokens:
+        tshape = (wl.text_tokens, cfg.heads, cfg.head_dim)
+        text = (si.to_f64(si.draw(tshape, 0, 0, 0, si.TEXT_K, cfg.torch_dtype)),
+                si.to_f64(si.draw(tshape, 0, 0, 0, si.TEXT_V, cfg.torch_dtype)))
     lq, lkv = q.shape[0], orc.n_vis() * f
+
+    def layer_pass(rows):
+        orc.chunk_attention(q, k, v, rows=rows)
+        if text is not None:
+            so.cross_attention(q, text[0], text[1], rows=rows)
+
     # grow the row sample until one call takes about a third of the budget (each call also ropes
     # every visible key, a fixed cost), then repeat that call until the budget is spent
     n = min(lq, 64)
     while True:
         rows = np.linspace(0, lq - 1, n).astype(np.int64)
         t0 = time.perf_counter()
-        orc.chunk_attention(q, k, v, rows=rows)
+        layer_pass(rows)
         dt = time.perf_counter() - t0
         if n == lq or dt >= target_s / 3:
             break
@@ -272,15 +294,27 @@ def cpu_baseline(runner, target_s):
     reps, total = 1, dt
     while total < target_s:
         t0 = time.perf_counter()
-        orc.chunk_attention(q, k, v, rows=rows)
+        layer_pass(rows)
         total += time.perf_counter() - t0
         reps += 1
     dt = total / reps
-    flops = 4.0 * len(rows) * lkv * cfg.head_dim * cfg.heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "cpu_model": cpu_model, "host_cpus": len(os.sched_getaffinity(0)), "blas": blas,
-            "sample": f"one steady {wl.name} pass (Lkv={lkv}), {len(rows)} of {lq} query rows x {cfg.heads} heads, "
-                      f"fp64 NumPy incl. RoPE of the visible keys; {reps} call(s), {total:.1f} s"}
+    keys = lkv + (wl.text_tokens or 0)
+    flops = 4.0 * len(rows) * keys * cfg.head_dim * cfg.heads
+    what = "self attention" + (f" + cross attention over {wl.text_tokens} text tokens" if text is not None else "")
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "cpu_model": cpu_model, "host_cpus": len(os.sched_getaffinity(0)), "blas": blas,
+           "sample": f"one steady {wl.name} layer-pass ({what}; Lkv={lkv}), {len(rows)} of {lq} query rows x "
+                     f"{cfg.heads} heads, fp64 NumPy incl. RoPE of the visible keys; {reps} call(s), {total:.1f} s"}
+    # one whole layer-pass at the sampled rate (the RoPE of the visible keys, a fixed cost per call,
+    # is scaled with the rows, so this overstates the full pass slightly when the sample is partial)
+    layer_pass_s = dt * lq / len(rows)
+    res["layer_pass_s"] = round(layer_pass_s, 3)
+    units = wl.layers * wl.passes
+    res["per_chunk_s"] = round(layer_pass_s * units, 2)
+    if units > 1:
+        res["per_chunk_note"] = (f"extrapolated: one layer-pass x {wl.layers} layers x {wl.passes} passes per chunk "
+                                 f"(= {units} layer-passes); the oracle's append is a list copy and is not timed")
+    return res
 
 
 def block_causal_leg(runner, args):
@@ -407,15 +441,25 @@ def hbm_leg(runner, reps=10):
     return res
 
 
-def traffic_from_profile(wl_name, per_launch_algo_bytes):
-    """HBM bytes per attention launch from committed rocprofv3 counters, if taken on the current kernel."""
-    p = os.path.join(ROOT, "profiles", f"attn_bf16_{wl_name}_counters.json")
-    if not os.path.exists(p):
-        return None
-    d = json.load(open(p))
-    if d.get("kernel_sha") != kernel_sha("attn_bf16.hip"):
-        return None
-    return d.get("hbm_bytes_per_dispatch")
+def attention_shape(cfg):
+    """What fixes the attention launch a workload times (grid, kernel shape, key ranges at steady
+    state): heads, head_dim, query rows and visible keys."""
+    f = cfg.tokens_per_frame
+    return {"heads": cfg.heads, "head_dim": cfg.head_dim, "lq": cfg.chunk_frames * f, "lkv": cfg.window_frames * f}
+
+
+def traffic_from_profile(cfg):
+    """HBM bytes per attention launch from committed rocprofv3 counters taken on the same kernel
+    code (hash of the source and its headers) at the same attention shape, else None.  Returns
+    (bytes, file name)."""
+    import glob
+    want = attention_shape(cfg)
+    sha = kernel_sha("attn_bf16.hip")
+    for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "attn_bf16_*_counters.json"))):
+        d = json.load(open(p))
+        if d.get("kernel_sha") == sha and d.get("shape") == want:
+            return d.get("hbm_bytes_per_dispatch"), os.path.basename(p)
+    return None, None
 
 
 def main():
@@ -500,9 +544,13 @@ def main():
     peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_VECTOR_PEAK_TFLOPS
     roof = {"bound": "mfma" if bf16 else "alu", "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(attn_tflops / peak, 4),
-            "traffic": traffic_from_profile(wl.name, None), "kernel": "attn_bf16_vt_kernel" if bf16 else "attn_f32_kernel",
+            "traffic": None, "kernel": "attn_bf16_vt_kernel" if bf16 else "attn_f32_kernel",
             "avg_kernel_ms": round(attn_ms, 4), "algorithmic_flop_per_launch": attn_flop}
     if bf16:
+        roof["traffic"], src = traffic_from_profile(cfg)
+        if src:
+            roof["traffic_source"] = (f"profiles/{src}: FETCH_SIZE + WRITE_SIZE per dispatch, calibrated, taken on "
+                                      f"the same kernel code at the same attention shape")
         roof["box_formula_peak"] = box_peak(torch)
     out = {
         "metric": "chunk-attention TFLOP/s + % bf16 MFMA peak; cache-update GB/s; per-chunk ms",
@@ -571,12 +619,12 @@ def main():
         out["constancy"] = {"chunks": wl.n_chunks, "steady_from_chunk": args.warmup, "window": n50,
                             "first_steady_ms": round(first, 3), "last_ms": round(last, 3),
                             "last_over_first": round(last / first, 4), "memory": mem}
-    if wl.layers == 1 and not args.no_legs:
+    if not args.no_legs:
         out["hbm_back_to_back"] = hbm_leg(r)
-    if bf16 and wl.layers == 1 and not args.no_legs:
+    if bf16 and not args.no_legs:
         out["block_causal"] = block_causal_leg(r, args)
         out["guidance_batch"] = guidance_leg(r)
-    if not args.no_cpu_baseline and wl.layers == 1:
+    if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 4
+#define SKV_ABI_VERSION 5
 
 typedef enum {
   SKV_OK = 0,
@@ -123,7 +123,11 @@ skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_
 skv_status kv_cache_init(const skv_config* cfg, void* k_store, void* v_store, void* workspace,
                          skv_cache** out);
 
-/* Forget every frame (counters to zero) and clear the poisoned flag. */
+/* Start a new stream on the same stores: forget every frame (counters to zero,
+ * nothing on the device is touched) and clear the poisoned flag.  [ABot-stream]
+ * "一次流式生成的完整链路": reset_stream() rebuilds the KV caches for a new
+ * stream, while a prompt change (set_prompts) rebuilds only the text cache and
+ * keeps the history, so a prompt swap never calls this.  Errors: SKV_ERR_NULL. */
 skv_status kv_cache_reset(skv_cache* cache);
 
 /* Free the host handle (device memory stays the caller's). NULL is a no-op. */
@@ -138,7 +142,10 @@ skv_status kv_cache_destroy(skv_cache* cache);
 skv_status kv_cache_append_evict(skv_cache* cache, const void* k, const void* v, int32_t n_frames,
                                  void* stream);
 
-/* 3D rotary embedding of x_in [n_frames*F, H, D] into x_out (may alias x_in).
+/* 3D rotary embedding of x_in [n_frames*F, H, D] into x_out (may alias x_in)
+ * ([LB-src] "改造③因果 RoPE 定位": a chunk's frames are rotated from start_frame on,
+ * so they continue the absolute time axis of the frames before them; [ABot-stream]
+ * 机制三: relative ids, the chunk takes the last slots of the visible window).
  * Token (frame i, row r, col w) is rotated at positions (t_i, r, w): head_dim
  * is split [time | height | width] and each adjacent pair (x_2k, x_2k+1) turns
  * by position * theta^(-2k/d_axis).  ABS: t_i = start_frame + i (start_frame >= 0).
@@ -155,9 +162,12 @@ skv_status rope_apply(const skv_cache* cache, const void* x_in, void* x_out, int
 skv_status rope_apply_qk(const skv_cache* cache, const void* q_in, void* q_out, const void* k_in, void* k_out,
                          int32_t n_frames, int64_t start_frame, void* stream);
 
-/* REL only: rotate the visible history k_raw (sinks, then the visible ring
+/* REL only ([ABot-stream] 机制三: the cache keeps un-rotated keys and only the
+ * visible window is rotated, at ids counted from the window's start and clamped
+ * to [0, window-1]): rotate the visible history k_raw (sinks, then the visible ring
  * frames oldest first) at time ids 0..n_vis-c-1 into the workspace, once per
- * chunk; its result serves every pass until the next append or reset. */
+ * chunk; its result serves every pass until the next append or reset.
+ * Errors: SKV_ERR_STATE in ABS mode or under fused rotation. */
 skv_status rope_apply_window(skv_cache* cache, void* stream);
 
 /* Stage the current chunk's values v_cur [c*F, H, D] in the workspace, in the
@@ -248,11 +258,30 @@ skv_status cross_attention_cached(const void* q, int32_t n_q, const void* store,
 /* Host-side bookkeeping of the handle. */
 skv_status kv_cache_info(const skv_cache* cache, kv_cache_info_t* info);
 
-/* Logical snapshot: copy the cached frames oldest first (sinks, then ring in
- * append order) into k_out/v_out [n_cached*F, H, D] (device) and their frame
- * ids into frame_ids_host[n_cached] (host; may be NULL).  Enqueued on stream. */
+/* Logical snapshot: the cache as the pages describe it ([LB-fast] "3. KV 缓存
+ * 滚动窗口" and [LB-causal] "Attention Sink": the first S frames, then the most
+ * recent frames, oldest first), copied into k_out/v_out [n_cached*F, H, D]
+ * (device; keys as stored: rotated in ABS mode and under fused rotation, raw in
+ * REL mode) with their frame ids in frame_ids_host[n_cached] (host; may be NULL;
+ * kv_cache_info gives n_cached).  The ids are filled before returning; the copies
+ * are enqueued on stream.  Errors: SKV_ERR_NULL / SKV_ERR_ALIGN on k_out, v_out;
+ * SKV_ERR_STATE on a poisoned handle. */
 skv_status kv_cache_gather(const skv_cache* cache, void* k_out, void* v_out, int64_t* frame_ids_host,
                            void* stream);
+
+/* Restore a snapshot taken with kv_cache_gather, on a handle of the same
+ * configuration (a stream resumed where it stopped; [ABot-stream] "一次流式生成的
+ * 完整链路": a stream keeps its KV history until reset_stream).  k, v: the gathered
+ * [n_frames*F, H, D] device tensors; frame_ids_host: the n_frames gathered ids.
+ * Each frame goes back to the slot its id maps to, so the handle afterwards holds
+ * what it held when gathered (n_appended = last id + 1; bytes, slots and the
+ * visible ranges identical, and with them every later result).  n_frames == 0
+ * leaves an empty cache (as kv_cache_reset).  REL mode needs rope_apply_window
+ * again before the next attention.  Errors: SKV_ERR_NULL / SKV_ERR_ALIGN on
+ * pointers; SKV_ERR_SHAPE when the ids are not exactly the ones kv_cache_gather
+ * reports for n_appended = last id + 1; SKV_ERR_STATE on a poisoned handle. */
+skv_status kv_cache_restore(skv_cache* cache, const void* k, const void* v, const int64_t* frame_ids_host,
+                            int32_t n_frames, void* stream);
 
 /* Many chunks at once under the sink + window block-causal mask ([ABot-stream]
  * 机制二: a chunk's queries see their own chunk and the window of earlier chunks,
@@ -295,6 +324,13 @@ skv_status block_causal_attention(const skv_config* cfg, const void* q, const vo
 skv_status sampler_step(const void* x_t, const void* v_cond, const void* v_uncond, double cfg_scale,
                         const void* noise, int64_t n, double sigma, double sigma_next, int32_t dtype,
                         void* x0_out, void* x_next_out, void* stream);
+
+/* Test hook for the failure path: the next n launches or device copies the
+ * library makes (any entry point) report a HIP failure without launching
+ * anything, as a failed launch would (SKV_ERR_HIP; a handle's call is then
+ * poisoned until kv_cache_reset).  n <= 0 disarms it.  Process-wide; for tests
+ * of the error handling only, no GPU work is involved. */
+void skv_debug_fail_launches(int32_t n);
 
 #ifdef __cplusplus
 }

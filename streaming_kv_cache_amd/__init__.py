@@ -27,6 +27,7 @@ EXPORTED = (
     "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v", "sampler_step",
     "chunk_attention_batch", "block_causal_workspace_bytes", "block_causal_attention",
     "text_cache_bytes", "text_cache_prepare", "cross_attention_cached", "rope_apply_qk", "kv_cache_prepare_pass",
+    "kv_cache_restore", "skv_debug_fail_launches",
 )
 
 
@@ -77,6 +78,8 @@ def _load() -> ctypes.CDLL:
         "cross_attention": ([vp, i32, vp, vp, i32, i32, i32, i32, vp, vp], st),
         "kv_cache_info": ([vp, ctypes.POINTER(KvCacheInfo)], st),
         "kv_cache_gather": ([vp, vp, vp, ctypes.POINTER(ctypes.c_int64), vp], st),
+        "kv_cache_restore": ([vp, vp, vp, ctypes.POINTER(ctypes.c_int64), i32, vp], st),
+        "skv_debug_fail_launches": ([i32], None),
         "kv_cache_stage_v": ([vp, vp, i32, vp], st),
         "chunk_attention_batch": ([ctypes.POINTER(vp), i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                    i32, ctypes.POINTER(vp), vp], st),
@@ -277,6 +280,21 @@ class KVCache:
         if n:
             _check(lib.kv_cache_gather(self._h, _ptr(k), _ptr(v), ids, _stream(stream)), "kv_cache_gather")
         return k, v, [int(ids[i]) for i in range(n)]
+
+    def restore(self, k: torch.Tensor, v: torch.Tensor, frame_ids, stream=None) -> None:
+        """Put back a snapshot from gather(): afterwards the cache holds exactly what it held then."""
+        n = len(frame_ids)
+        ids = (ctypes.c_int64 * max(n, 1))(*[int(i) for i in frame_ids])
+        if n:
+            self._tensor(k, n, "k")
+            self._tensor(v, n, "v")
+        _check(lib.kv_cache_restore(self._h, _ptr(k if n else None), _ptr(v if n else None), ids, n,
+                                    _stream(stream)), "kv_cache_restore")
+
+
+def debug_fail_launches(n: int) -> None:
+    """Test hook: the next n launches of the library report a HIP failure without launching."""
+    lib.skv_debug_fail_launches(int(n))
 
 
 def chunk_attention_batch(caches, qs, ks, vs, outs=None, stream=None):

@@ -2,6 +2,7 @@
 // ring bookkeeping and kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <new>
@@ -22,6 +23,18 @@ struct skv_cache {
 };
 
 namespace {
+
+// Test hook (skv_debug_fail_launches): the next n launches report a failure without launching.
+std::atomic<int32_t> g_fail_launches{0};
+
+// Every kernel launch and device copy of the library goes through here.
+template <class F>
+hipError_t gate(F&& launch) {
+  int32_t n = g_fail_launches.load();
+  while (n > 0)
+    if (g_fail_launches.compare_exchange_weak(n, n - 1)) return hipErrorLaunchFailure;
+  return launch();
+}
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
@@ -111,16 +124,17 @@ skv::WriteArgs stage_args(const skv_cache* c, const void* v_cur) {
 }
 
 skv_status stage_v(skv_cache* c, const void* v_cur, void* stream) {
-  return launched(c, skv::launch_write_kv(stage_args(c, v_cur), c->g.elt, (hipStream_t)stream));
+  return launched(c, gate([&] { return skv::launch_write_kv(stage_args(c, v_cur), c->g.elt, (hipStream_t)stream); }));
 }
 
 // A rotary launch and the staging of v_cur: one grid in bf16, two launches in fp32.
 skv_status rope_and_stage(skv_cache* c, const skv::RopeLaunch& L, const void* v_cur, void* stream) {
   const skv::WriteArgs w = stage_args(c, v_cur);
-  if (c->g.dtype == SKV_BF16) return launched(c, skv::launch_prepare_pass(L, w, (hipStream_t)stream));
-  const skv_status st = launched(c, skv::launch_rope(L, (hipStream_t)stream));
+  if (c->g.dtype == SKV_BF16)
+    return launched(c, gate([&] { return skv::launch_prepare_pass(L, w, (hipStream_t)stream); }));
+  const skv_status st = launched(c, gate([&] { return skv::launch_rope(L, (hipStream_t)stream); }));
   if (st != SKV_OK) return st;
-  return launched(c, skv::launch_write_kv(w, c->g.elt, (hipStream_t)stream));
+  return launched(c, gate([&] { return skv::launch_write_kv(w, c->g.elt, (hipStream_t)stream); }));
 }
 
 // Rotary launch over n_frames frames of a token-major tensor (or the store, via runs).
@@ -269,7 +283,7 @@ skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int
     skv::RopeLaunch L = rope_launch(g, token_view(g, k), store_view(g, c->k_store), n_frames, c->ring.T, -1);
     L.nruns = nruns;
     for (int i = 0; i < 3; ++i) L.runs[i] = i < nruns ? runs[i] : skv::FrameRun{0, 0, 0, 0};
-    st = launched(c, skv::launch_rope(L, (hipStream_t)stream));
+    st = launched(c, gate([&] { return skv::launch_rope(L, (hipStream_t)stream); }));
     if (st != SKV_OK) return st;
   }
   skv::WriteArgs wa{};
@@ -289,7 +303,7 @@ skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int
   wa.D = g.D;
   wa.n_tok = n_frames * g.F;
   wa.row_pad = 0;
-  st = launched(c, skv::launch_write_kv(wa, g.elt, (hipStream_t)stream));
+  st = launched(c, gate([&] { return skv::launch_write_kv(wa, g.elt, (hipStream_t)stream); }));
   if (st != SKV_OK) return st;
   c->ring.T += n_frames;
   c->window_ready = false;
@@ -333,7 +347,7 @@ static skv_status rope_tensors(const skv_cache* cc, const void* const* in, void*
   skv::RopeLaunch L;
   const skv_status st = rope_plan(c, in, out, n, n_frames, start_frame, &L);
   if (st != SKV_OK) return st;
-  return launched(c, skv::launch_rope(L, (hipStream_t)stream));
+  return launched(c, gate([&] { return skv::launch_rope(L, (hipStream_t)stream); }));
 }
 
 skv_status rope_apply(const skv_cache* cache, const void* x_in, void* x_out, int32_t n_frames, int64_t start_frame,
@@ -378,7 +392,7 @@ skv_status rope_apply_window(skv_cache* c, void* stream) {
     L.nruns = p.n_runs;
     for (int i = 0; i < p.n_runs; ++i)
       L.runs[i] = skv::FrameRun{p.runs[i].logical0, p.runs[i].frames, p.runs[i].slot0, p.runs[i].logical0};
-    st = launched(c, skv::launch_rope(L, (hipStream_t)stream));
+    st = launched(c, gate([&] { return skv::launch_rope(L, (hipStream_t)stream); }));
     if (st != SKV_OK) return st;
   }
   c->window_ready = true;
@@ -491,7 +505,8 @@ skv_status chunk_attention_batch(const skv_cache* const* caches, int32_t n_cache
     skv_status st = SKV_OK;
     if (cs[i]->g.fused) {
       const skv::RopeLaunch L = fused_rope_launch(cs[i], q[i], k_cur[i]);
-      st = stage ? rope_and_stage(cs[i], L, v_cur[i], stream) : launched(cs[i], skv::launch_rope(L, (hipStream_t)stream));
+      st = stage ? rope_and_stage(cs[i], L, v_cur[i], stream)
+                 : launched(cs[i], gate([&] { return skv::launch_rope(L, (hipStream_t)stream); }));
     } else if (stage) {
       st = stage_v(cs[i], v_cur[i], stream);
     }
@@ -501,9 +516,10 @@ skv_status chunk_attention_batch(const skv_cache* const* caches, int32_t n_cache
   const skv::Geometry& g = cs[0]->g;
   hipError_t e = hipSuccess;
   if (g.dtype == SKV_BF16) {
-    e = skv::launch_attention_bf16_vt(ab, g.D, (hipStream_t)stream);
+    e = gate([&] { return skv::launch_attention_bf16_vt(ab, g.D, (hipStream_t)stream); });
   } else {
-    for (int i = 0; i < n_caches && e == hipSuccess; ++i) e = skv::launch_attention_f32(ab.b[i], g.D, (hipStream_t)stream);
+    for (int i = 0; i < n_caches && e == hipSuccess; ++i)
+      e = gate([&] { return skv::launch_attention_f32(ab.b[i], g.D, (hipStream_t)stream); });
   }
   skv_status st = SKV_OK;
   for (int i = 0; i < n_caches; ++i) {
@@ -541,8 +557,8 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
   a.seg[0] = skv::KvSeg{k_text, v_text, (int64_t)head_dim, (int64_t)heads * head_dim,
                         (int64_t)head_dim, (int64_t)heads * head_dim, 1, n_text, 0};
   for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
-  const hipError_t e = dtype == SKV_BF16 ? skv::launch_attention_bf16_tokv(a, head_dim, (hipStream_t)stream)
-                                         : skv::launch_attention_f32(a, head_dim, (hipStream_t)stream);
+  const hipError_t e = dtype == SKV_BF16 ? gate([&] { return skv::launch_attention_bf16_tokv(a, head_dim, (hipStream_t)stream); })
+                                         : gate([&] { return skv::launch_attention_f32(a, head_dim, (hipStream_t)stream); });
   return e == hipSuccess ? SKV_OK : SKV_ERR_HIP;
 }
 
@@ -594,10 +610,11 @@ skv_status text_cache_prepare(const void* k_text, const void* v_text, int32_t n_
   TextLayout L;
   if ((st = text_layout(n_text, heads, head_dim, dtype, &L)) != SKV_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
-  if (hipMemcpyAsync(store, k_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s) != hipSuccess) return SKV_ERR_HIP;
+  if (gate([&] { return hipMemcpyAsync(store, k_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s); }) != hipSuccess)
+    return SKV_ERR_HIP;
   char* vdst = (char*)store + L.vt_off;
   if (dtype != SKV_BF16)
-    return hipMemcpyAsync(vdst, v_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s) == hipSuccess ? SKV_OK
+    return gate([&] { return hipMemcpyAsync(vdst, v_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s); }) == hipSuccess ? SKV_OK
                                                                                                  : SKV_ERR_HIP;
   // values -> V^T rows [h][d][key], keys past n_text zero up to the padded row length
   skv::WriteArgs wa{};
@@ -614,7 +631,7 @@ skv_status text_cache_prepare(const void* k_text, const void* v_text, int32_t n_
   wa.D = head_dim;
   wa.n_tok = n_text;
   wa.row_pad = (int32_t)L.pad;
-  return skv::launch_write_kv(wa, 2, s) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+  return gate([&] { return skv::launch_write_kv(wa, 2, s); }) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
 }
 
 skv_status cross_attention_cached(const void* q, int32_t n_q, const void* store, int32_t n_text, int32_t heads,
@@ -644,11 +661,11 @@ skv_status cross_attention_cached(const void* q, int32_t n_q, const void* store,
     // K token-major as given; V^T rows of L.pad keys per (head, dim)
     a.seg[0] = skv::KvSeg{store, vsrc, (int64_t)head_dim, (int64_t)heads * head_dim, (int64_t)head_dim * L.pad, 1,
                           L.pad, n_text, 1};
-    return skv::launch_attention_bf16_vt(ab, head_dim, s) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+    return gate([&] { return skv::launch_attention_bf16_vt(ab, head_dim, s); }) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
   }
   a.seg[0] = skv::KvSeg{store, vsrc, (int64_t)head_dim, (int64_t)heads * head_dim, (int64_t)head_dim,
                         (int64_t)heads * head_dim, 1, n_text, 0};
-  return skv::launch_attention_f32(a, head_dim, s) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+  return gate([&] { return skv::launch_attention_f32(a, head_dim, s); }) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
 }
 
 // Many-chunk attention: checks shared by the size query and the call.
@@ -703,7 +720,7 @@ skv_status block_causal_attention(const skv_config* cfg, const void* q, const vo
   wa.D = g.D;
   wa.n_tok = n_frames * g.F;
   wa.row_pad = (int32_t)row_pad;
-  if (skv::launch_write_kv(wa, g.elt, (hipStream_t)stream) != hipSuccess) return SKV_ERR_HIP;
+  if (gate([&] { return skv::launch_write_kv(wa, g.elt, (hipStream_t)stream); }) != hipSuccess) return SKV_ERR_HIP;
   skv::AttnBatch ab{};
   ab.nb = 1;
   skv::AttnArgs& a = ab.b[0];
@@ -722,7 +739,9 @@ skv_status block_causal_attention(const skv_config* cfg, const void* q, const vo
   a.mc = g.c;
   a.mS = g.S;
   a.mW = g.W;
-  return skv::launch_attention_bf16_masked(ab, g.D, (hipStream_t)stream) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
+  return gate([&] { return skv::launch_attention_bf16_masked(ab, g.D, (hipStream_t)stream); }) == hipSuccess
+             ? SKV_OK
+             : SKV_ERR_HIP;
 }
 
 skv_status sampler_step(const void* x_t, const void* v_cond, const void* v_uncond, double cfg_scale,
@@ -742,7 +761,7 @@ skv_status sampler_step(const void* x_t, const void* v_cond, const void* v_uncon
   if (n == 0) return SKV_OK;
   skv::SamplerArgs a{x_t, v_cond, v_uncond, x_next_out ? noise : nullptr, x0_out, x_next_out, n,
                      cfg_scale, sigma, sigma_next};
-  return skv::launch_sampler(a, dtype == SKV_BF16 ? 2 : 4, (hipStream_t)stream) == hipSuccess ? SKV_OK
+  return gate([&] { return skv::launch_sampler(a, dtype == SKV_BF16 ? 2 : 4, (hipStream_t)stream); }) == hipSuccess ? SKV_OK
                                                                                              : SKV_ERR_HIP;
 }
 
@@ -769,7 +788,9 @@ skv_status kv_cache_gather(const skv_cache* cc, void* k_out, void* v_out, int64_
   }
   const skv::TokView src[2] = {store_view(g, c->k_store), store_view(g, c->k_store)};
   const skv::TokView dst[2] = {token_view(g, k_out), token_view(g, k_out)};
-  st = launched(c, skv::launch_copy_frames(src, dst, 1, runs, nruns, n, g.F, g.H, g.D, g.elt, (hipStream_t)stream));
+  st = launched(c, gate([&] {
+                  return skv::launch_copy_frames(src, dst, 1, runs, nruns, n, g.F, g.H, g.D, g.elt, (hipStream_t)stream);
+                }));
   if (st != SKV_OK) return st;
   skv::WriteArgs va{};
   va.k_dst = v_out;
@@ -786,7 +807,65 @@ skv_status kv_cache_gather(const skv_cache* cc, void* k_out, void* v_out, int64_
   va.D = g.D;
   va.n_tok = n * g.F;
   va.row_pad = 0;
-  return launched(c, skv::launch_vt_to_tok(va, g.elt, (hipStream_t)stream));
+  return launched(c, gate([&] { return skv::launch_vt_to_tok(va, g.elt, (hipStream_t)stream); }));
 }
+
+skv_status kv_cache_restore(skv_cache* c, const void* k, const void* v, const int64_t* frame_ids_host,
+                            int32_t n_frames, void* stream) {
+  skv_status st = check_handle(c);
+  if (st != SKV_OK) return st;
+  if (n_frames < 0) return SKV_ERR_SHAPE;
+  const skv::Geometry& g = c->g;
+  skv::RingState r;
+  if (n_frames > 0) {
+    if ((st = check_ptr(k)) != SKV_OK) return st;
+    if ((st = check_ptr(v)) != SKV_OK) return st;
+    if (!frame_ids_host) return SKV_ERR_NULL;
+    // the ids must be exactly the ones kv_cache_gather reports for T = last id + 1
+    if (frame_ids_host[n_frames - 1] < 0) return SKV_ERR_SHAPE;
+    r.T = frame_ids_host[n_frames - 1] + 1;
+    if (r.n_cached(g) != n_frames) return SKV_ERR_SHAPE;
+    for (int i = 0; i < n_frames; ++i)
+      if (frame_ids_host[i] != r.cached_frame(g, i)) return SKV_ERR_SHAPE;
+    // logical frame i -> its slot, merged into runs of consecutive slots (sinks, ring part a, ring part b)
+    skv::FrameRun runs[3];
+    int nruns = 0;
+    for (int i = 0; i < n_frames; ++i) {
+      const int slot = r.slot_of(g, frame_ids_host[i]);
+      if (nruns > 0 && runs[nruns - 1].dst0 + runs[nruns - 1].count == slot) {
+        ++runs[nruns - 1].count;
+      } else {
+        if (nruns == 3) return SKV_ERR_STATE;  // cannot happen: sinks + at most two ring runs
+        runs[nruns++] = skv::FrameRun{i, 1, i, slot};
+      }
+    }
+    // the bytes go back as they were gathered (keys stay as stored: rotated or raw), K rows + V^T
+    skv::WriteArgs wa{};
+    wa.k_src = k;
+    wa.v_src = v;
+    wa.tok_stride = (int64_t)g.H * g.D;
+    wa.head_stride = g.D;
+    wa.k_dst = c->k_store;
+    wa.k_hs = (int64_t)g.W * g.F * g.D;
+    wa.vt_dst = c->v_store;
+    wa.vt_hs = (int64_t)g.D * vt_row(g);
+    wa.vt_ds = vt_row(g);
+    for (int i = 0; i < 3; ++i) wa.runs[i] = i < nruns ? runs[i] : skv::FrameRun{0, 0, 0, 0};
+    wa.nruns = nruns;
+    wa.F = g.F;
+    wa.H = g.H;
+    wa.D = g.D;
+    wa.n_tok = n_frames * g.F;
+    wa.row_pad = 0;
+    st = launched(c, gate([&] { return skv::launch_write_kv(wa, g.elt, (hipStream_t)stream); }));
+    if (st != SKV_OK) return st;
+  }
+  c->ring.T = r.T;
+  c->window_ready = false;
+  c->v_staged = false;
+  return SKV_OK;
+}
+
+void skv_debug_fail_launches(int32_t n) { g_fail_launches.store(n > 0 ? n : 0); }
 
 }  // extern "C"

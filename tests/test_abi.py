@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert skv.lib.skv_abi_version() == 4
+    assert skv.lib.skv_abi_version() == 5
     for code in range(7):
         assert skv.status_string(code)
     assert skv.status_string(99) == "unknown status"
