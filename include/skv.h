@@ -304,6 +304,21 @@ skv_status block_causal_workspace_bytes(const skv_config* cfg, int32_t n_frames,
 skv_status block_causal_attention(const skv_config* cfg, const void* q, const void* k, const void* v,
                                   int32_t n_frames, int32_t q_frame0, void* workspace, void* out, void* stream);
 
+/* block_causal_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same result, with the workspace taken from a static device array the library
+ * owns (SKV_NOALLOC_SCRATCH_BYTES = 64 MiB on each device it runs on, held until
+ * the process ends) instead of a caller's buffer.  It allocates nothing: the
+ * array's address is looked up once per device on the first call (with that
+ * device current).  Every call on a device uses that device's one array, so
+ * calls that overlap on one device race (one at a time per device, e.g. one
+ * stream).  Arguments and errors are those of block_causal_attention, plus
+ * SKV_ERR_SHAPE when block_causal_workspace_bytes(cfg, n_frames) exceeds
+ * SKV_NOALLOC_SCRATCH_BYTES and SKV_ERR_HIP when the array cannot be located. */
+#define SKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+skv_status block_causal_attention_noalloc(const skv_config* cfg, const void* q, const void* k, const void* v,
+                                          int32_t n_frames, int32_t q_frame0, void* out, void* stream);
+
 /* One step of the few-step sampler between attention passes ([LB-fast]
  * "2. 4 步采样": the forward gives a flow-matching velocity, x0 is recovered in
  * one step and re-noised to the next, smaller timestep unless it was the last;

@@ -27,7 +27,7 @@ EXPORTED = (
     "cross_attention", "kv_cache_info", "kv_cache_gather", "kv_cache_stage_v", "sampler_step",
     "chunk_attention_batch", "block_causal_workspace_bytes", "block_causal_attention",
     "text_cache_bytes", "text_cache_prepare", "cross_attention_cached", "rope_apply_qk", "kv_cache_prepare_pass",
-    "kv_cache_restore", "skv_debug_fail_launches",
+    "kv_cache_restore", "skv_debug_fail_launches", "block_causal_attention_noalloc",
 )
 
 
@@ -85,6 +85,7 @@ def _load() -> ctypes.CDLL:
                                    i32, ctypes.POINTER(vp), vp], st),
         "block_causal_workspace_bytes": ([ctypes.POINTER(SkvConfig), i32, ctypes.POINTER(ctypes.c_size_t)], st),
         "block_causal_attention": ([ctypes.POINTER(SkvConfig), vp, vp, vp, i32, i32, vp, vp, vp], st),
+        "block_causal_attention_noalloc": ([ctypes.POINTER(SkvConfig), vp, vp, vp, i32, i32, vp, vp], st),
         "sampler_step": ([vp, vp, vp, ctypes.c_double, vp, i64, ctypes.c_double, ctypes.c_double, i32, vp, vp, vp],
                          st),
         "text_cache_bytes": ([i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)], st),
@@ -344,6 +345,26 @@ def block_causal_attention(cfg: Config, q: torch.Tensor, k: torch.Tensor, v: tor
     c = cfg.c_struct()
     _check(lib.block_causal_attention(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), n, int(q_frame0), _ptr(workspace),
                                       _ptr(out), _stream(stream)), "block_causal_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def block_causal_attention_noalloc(cfg: Config, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                                   q_frame0: int = 0, stream=None) -> torch.Tensor:
+    """block_causal_attention with the workspace in the library's static device array (the call allocates
+    nothing; ``out`` is the caller's).  At most NOALLOC_SCRATCH_BYTES of workspace (see skv.h)."""
+    f = cfg.tokens_per_frame
+    n = k.shape[0] // f
+    for name, t, rows in (("k", k, n * f), ("v", v, n * f), ("q", q, (n - q_frame0) * f), ("out", out, (n - q_frame0) * f)):
+        if tuple(t.shape) != (rows, cfg.heads, cfg.head_dim) or t.dtype != cfg.torch_dtype or not t.is_cuda \
+                or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous {cfg.torch_dtype} CUDA tensor of shape "
+                             f"{(rows, cfg.heads, cfg.head_dim)}")
+    c = cfg.c_struct()
+    _check(lib.block_causal_attention_noalloc(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), n, int(q_frame0), _ptr(out),
+                                              _stream(stream)), "block_causal_attention_noalloc")
     return out
 
 

@@ -23,7 +23,8 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["skv_core.cpp", "skv_lib.cpp", "cache_kernels.hip", "vt_kernels.hip", "attn_f32.hip", "attn_bf16.hip", "sampler_kernels.hip"]
+SOURCES = ["skv_core.cpp", "skv_lib.cpp", "cache_kernels.hip", "vt_kernels.hip", "attn_f32.hip", "attn_bf16.hip",
+           "sampler_kernels.hip", "noalloc.hip"]
 
 
 def hipcc() -> str:
