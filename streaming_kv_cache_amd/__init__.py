@@ -187,7 +187,7 @@ class KVCache:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
+        if h is not None and h.value and lib is not None:   # lib is None during interpreter shutdown
             lib.kv_cache_destroy(h)
             self._h = None
 

@@ -419,19 +419,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
   const int q_base = qt * BM + wave * 32;
   const float sl2 = a.sl2;
 
-  // Q^T, pre-multiplied by softmax scale * log2(e): scores come out in log2 units.
+  // Q^T, pre-multiplied by softmax scale * log2(e): scores come out in log2 units.  fetch_q issues
+  // the loads, scale_q (which waits for them) converts in place; the prologue issues the first K/V
+  // tiles in between, so the latencies of the query rows and of the first tiles overlap.
   bf16x8_t qreg[KSTEPS];
-  auto load_q = [&](const void* src) {
+  auto fetch_q = [&](const void* src) {
     const int qi = q_base + l32;
     const bool ok = qi < a.Lq;
     const uint16_t* qp = (const uint16_t*)src + ((int64_t)(ok ? qi : 0) * a.H + h) * D + 8 * hf;
 #pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qreg[ks] = __builtin_bit_cast(bf16x8_t, ok ? *(const u32x4_t*)(qp + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u});
+  };
+  auto scale_q = [&]() {
+#pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4_t v = ok ? *(const u32x4_t*)(qp + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+      u32x4_t v = __builtin_bit_cast(u32x4_t, qreg[ks]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(bf16_lo_to_f32(v[e]) * sl2, bf16_hi_to_f32(v[e]) * sl2);
       qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
+  };
+  auto load_q = [&](const void* src) {
+    fetch_q(src);
+    scale_q();
   };
   f32x16_t o[MBLK];
 #pragma unroll
@@ -520,12 +531,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       return;
     }
   }
-  // queries of the first tile (from the switch on: at q_alt)
+  // queries of the first tile (from the switch on: at q_alt); converted once the first tiles are issued
   if (alt_tiles <= 0) {
-    load_q(a.q_alt);
+    fetch_q(a.q_alt);
     alt_tiles = 1 << 30;
   } else {
-    load_q(a.q);
+    fetch_q(a.q);
   }
   int ksi = 0, krem = 0, k_rs_b = 0;
   const uint8_t* kp = nullptr;
@@ -680,6 +691,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       k0q[i] = key0;
       issue_v(i);
     }
+  scale_q();
 
   // P = exp2(S' - sub) for one 32-key half, packed to bf16 in B-operand order; returns the
   // row sum of the rounded values.
@@ -1090,7 +1102,16 @@ static hipError_t launch_vt(const AttnBatch& in, int D, hipStream_t stream) {
   // SKV_ATTN_WAVES=4 or 8 forces one shape (tests cover both on small inputs)
   const char* env = std::getenv("SKV_ATTN_WAVES");
   const int forced = (env && *env) ? std::atoi(env) : 0;
-  bool big = forced == 8 || (forced != 4 && rounds8 < rounds4);
+  // short key sequences (e.g. cross attention over a few hundred text tokens): a workgroup's
+  // prologue and pipeline fill are a large part of its life, and two 4-wave workgroups per CU
+  // overlap them where one 8-wave workgroup cannot (480P x 512 text tokens: 92 -> 88 us)
+  int seq_tiles = 0;
+  for (int i = 0; i < a.nb; ++i) {
+    int nt = 0;
+    for (int s_ = 0; s_ < a.b[i].nseg; ++s_) nt += (a.b[i].seg[s_].n + kBN - 1) / kBN;
+    seq_tiles = nt > seq_tiles ? nt : seq_tiles;
+  }
+  bool big = forced == 8 || (forced != 4 && !(!MASKED && seq_tiles <= 16) && rounds8 < rounds4);
   // split keys: SKV_ATTN_SPLIT=0 never, =1 whenever the buffers allow (tests), unset: grids that fill
   // at most half of one dispatch round
   int nsplit = 1;
