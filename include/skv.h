@@ -102,10 +102,13 @@ typedef struct skv_cache skv_cache; /* opaque host-side handle */
 int skv_abi_version(void);
 const char* skv_status_string(skv_status s);
 
-/* Bytes the caller must allocate for one K store and one V store (each
- * W*F*H*D elements of cfg->dtype) and for the workspace.  Physical layouts:
+/* Bytes the caller must allocate for each of the K store and the V store (one
+ * size for both: H*D*P elements of cfg->dtype, P = W*F rounded up to a multiple
+ * of 64) and for the workspace.  Physical layouts:
  *   K store  [H][W*F][D]   (head-major; slot s holds tokens [s*F, (s+1)*F));
- *   V store  [H][D][W*F]   (transposed per head, same token numbering);
+ *   V store  V transposed per head, same key numbering: bf16 in tiles of 64 keys,
+ *            [H][P/64][D][64] (element (h, d, key) at ((h*P/64 + key/64)*D + d)*64
+ *            + key%64), fp32 in rows [H][D][P];
  *   workspace: first (REL only) the rotated visible window [H][(W-c)*F][D] (with
  *   fused_rope instead: q at absolute ids, k_cur at absolute ids and, REL, q at
  *   slot ids, [c*F][H][D] each), then the staged current-chunk values [H][D][P]
@@ -171,8 +174,8 @@ skv_status rope_apply_qk(const skv_cache* cache, const void* q_in, void* q_out, 
 skv_status rope_apply_window(skv_cache* cache, void* stream);
 
 /* Stage the current chunk's values v_cur [c*F, H, D] in the workspace, in the
- * transposed layout the attention kernel reads (V^T[h][d][token], rows padded
- * with zeros to a multiple of 64 tokens).  chunk_attention does this itself when
+ * transposed layout the attention kernel reads (the V store's layout over c*F
+ * keys, padded with zeros to a multiple of 64 keys).  chunk_attention does this itself when
  * it is given v_cur; calling it separately lets a caller time or overlap it.
  * n_frames must equal c. */
 skv_status kv_cache_stage_v(skv_cache* cache, const void* v_cur, int32_t n_frames, void* stream);
@@ -237,11 +240,12 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
  * its note on the cross-attention cache; [ABot-stream] "一次流式生成的完整链路",
  * step 1: the 512-token text cache is built once, and a prompt change rebuilds
  * only it), so their layout is fixed once:
- * text_cache_prepare copies k_text and stores v_text transposed (V^T rows of the
- * keys, padded to a multiple of 64 with zeros) into `store`, a caller-allocated
+ * text_cache_prepare copies k_text and stores v_text transposed (the keys padded
+ * to a multiple of 64 with zeros) into `store`, a caller-allocated
  * device buffer of text_cache_bytes(...) bytes, 256-byte aligned.  bf16: the
  * copy of k_text [n_text, H, D] is followed, at the next 256-byte boundary, by
- * V^T [H][D][roundup(n_text, 64)]; fp32: copies of k_text and v_text back to back.
+ * V^T in tiles of 64 keys, [H][P/64][D][64] with P = roundup(n_text, 64) and the
+ * keys past n_text zero; fp32: copies of k_text and v_text back to back.
  * cross_attention_cached then attends q/out [n_q, H, D] over the store with the
  * same result definition as cross_attention (bf16: the matrix-core kernel of
  * chunk_attention, which reads V^T with direct-to-LDS loads).  The store is
@@ -296,7 +300,8 @@ skv_status kv_cache_restore(skv_cache* cache, const void* k, const void* v, cons
  * and sees key frame j iff j < e and (j < S or j >= e - (W - S)): exactly the keys a
  * chunk sees when it is streamed through a cache with S sinks and window W.
  * workspace: block_causal_workspace_bytes(cfg, n_frames) bytes of device memory
- * (the values are transposed there first).  Requires (n_frames - q_frame0) % c == 0.
+ * (the values are transposed there first, in the V store's bf16 tile layout).
+ * Requires (n_frames - q_frame0) % c == 0.
  * Errors: SKV_ERR_NULL / SKV_ERR_ALIGN on pointers; SKV_ERR_CONFIG for an invalid or
  * non-bf16 cfg; SKV_ERR_SHAPE for frame counts out of range or a sequence too long
  * for 32-bit offsets within one head. */

@@ -8,8 +8,8 @@
 // only the last tile of each range is partial.
 //
 // Three kernels:
-//   * attn_bf16_vt_kernel (the cache path): V arrives transposed (V^T[h][d][key],
-//     the layout the V store keeps); K rows and V^T tiles go global -> LDS with
+//   * attn_bf16_vt_kernel (the cache path): V arrives transposed, in the V store's
+//     tiles of 64 keys (V^T[h][key / 64][d][key % 64]); K rows and V^T tiles go global -> LDS with
 //     direct-to-LDS buffer loads into padded, conflict-free layouts.  Two shapes:
 //     4 waves x 32 query rows with two stages (two workgroups per CU), or 8 waves
 //     x 32 rows with four stages (one workgroup per CU); the host picks the one
@@ -559,25 +559,32 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       kq_off[i] = row * k_rs_b + c16;
     }
   };
-  int vsi = 0, vrem = 0, v_ds_b = 0, v_al16 = 1;
+  // V^T in 64-key tiles: the current range starts at position vph of the tile at vp; the tile
+  // iterator advances by whole tiles (v_so), so a lane's offset inside the range is fixed.
+  constexpr int VTILE_B = 2 * kVtKeys * D;  // bytes of one tile (every d of 64 keys)
+  int vsi = 0, vrem = 0, v_al16 = 1, vph = 0;
   const uint8_t* vp = nullptr;
-  
   int v_so = 0;
   __amdgpu_buffer_rsrc_t vrs = buf_rsrc(nullptr);
+  // byte offset from vp of the keys starting at range key r (a multiple of 8 when aligned), dim d
+  auto v_off = [&](int d, int r) -> int {
+    const int p = vph + r;
+    return (p >> 6) * VTILE_B + d * (2 * kVtKeys) + 2 * (p & 63);
+  };
   auto v_seg = [&](int s_) {
     const KvSeg sg = a.seg[MASKED ? 0 : s_];
-    const int start = seg_start(s_);
-    vp = (const uint8_t*)sg.v + 2 * ((int64_t)h * sg.v_hs + (int64_t)start * sg.v_rs);
+    const int pe = sg.v_phase + seg_start(s_);
+    vp = (const uint8_t*)sg.v + 2 * (int64_t)h * sg.v_hs + (int64_t)(pe >> 6) * VTILE_B;
+    vph = pe & 63;
     v_so = 0;
     vrs = buf_rsrc(vp);
-    v_ds_b = (int)(2 * sg.v_ds);
     vrem = seg_n(s_);
-    v_al16 = sg.v_al16 && (start & 7) == 0;
+    v_al16 = sg.v_al16 && (vph & 7) == 0;
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       int d, ch;
       v_lane(i, lane, d, ch);
-      vq_off[i] = d * v_ds_b + 16 * ch;
+      vq_off[i] = v_off(d, 8 * ch);
     }
   };
   k_seg(0);
@@ -592,8 +599,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
       k_so += skip * kBN * k_rs_b;
       kkey += skip * kBN;
       krem -= skip * kBN;
-      v_so += skip * 2 * kBN;
-      vp += skip * 2 * kBN;
+      v_so += skip * VTILE_B;
+      vp += skip * VTILE_B;
       vrem -= skip * kBN;
       skip = 0;
     } else {
@@ -658,20 +665,20 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
           int d, ch;
           v_lane(i, ln, d, ch);
           const int cc = 8 * ch < nk ? ch : 0;  // chunks past the range: valid data, P is 0
-          buf_lds16(vrs, dst + blk * 1024, d * v_ds_b + 16 * cc, v_so);
+          buf_lds16(vrs, dst + blk * 1024, v_off(d, 8 * cc), v_so);
         }
       }
     } else {
-      // ranges whose keys are not 16-byte aligned: element copies through registers
+      // ranges whose first key does not start a 16-byte piece: element copies through registers
       for (int idx = tid; idx < D * kBN; idx += NW * 64) {
         const int d = idx / kBN, e = idx % kBN;
         const int kk = e < nk ? e : 0;
-        ((uint16_t*)(dst + d * VP))[e] = *(const uint16_t*)(vp + (int64_t)d * v_ds_b + 2 * kk);
+        ((uint16_t*)(dst + d * VP))[e] = *(const uint16_t*)(vp + v_off(d, kk));
       }
     }
     vrem -= kBN;
-    vp += 2 * kBN;
-    v_so += 2 * kBN;
+    vp += VTILE_B;
+    v_so += VTILE_B;
     while (vrem <= 0 && ++vsi < nseg) v_seg(vsi);
   };
 

@@ -39,16 +39,25 @@ struct TokView {
   int64_t tok_stride, head_stride;
 };
 
+// Transposed bf16 values (V^T) are kept in tiles of kVtKeys keys: tile b of head h holds
+// V^T[h][d][64 b + j] for all d at h*hs + b*64*D + d*64 + j (16 KB for D = 128), so a write of
+// 64 keys and a read of one attention tile are whole, contiguous tiles when 64-aligned.
+constexpr int kVtKeys = 64;
+
 // One contiguous range of visible keys for the attention kernels.
-// Key j of the range, head h, dim d: K at k + j*k_rs + h*k_hs + d,
-// V at v + h*v_hs + j*v_rs + d*v_ds (token-major V: v_rs = H*D, v_ds = 1;
-// transposed V: v_rs = 1, v_ds = row length).
+// Key j of the range, head h, dim d: K at k + j*k_rs + h*k_hs + d.
+// V: token-major (fp32 and the cross-attention kernel): v + h*v_hs + j*v_rs + d*v_ds
+// (v_rs = H*D, v_ds = 1); transposed fp32 rows: v_rs = 1, v_ds = row length;
+// transposed bf16 (tiled, the cache-path kernel): v points at the tile that holds the range's
+// first key, which sits at position v_phase of it, so key j is at
+// v + h*v_hs + ((v_phase + j) / 64)*64*D + d*64 + (v_phase + j) % 64.
 struct KvSeg {
   const void* k;
   const void* v;
   int64_t k_hs, k_rs, v_hs, v_rs, v_ds;
   int32_t n;
-  int32_t v_al16;  // transposed V: row starts and the range start are 16-byte aligned
+  int32_t v_al16;   // transposed V: 16-byte pieces of 8 keys line up (row starts / v_phase + start)
+  int32_t v_phase;  // tiled bf16 V^T: position of the range's first key in its tile
 };
 
 struct AttnArgs {

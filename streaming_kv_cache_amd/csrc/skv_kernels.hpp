@@ -14,9 +14,12 @@ hipError_t launch_copy_frames(const TokView src[2], const TokView dst[2], int n_
 // Write-back of whole frames (K rows + transposed V) and current-chunk staging.
 // Sources are token-major [tokens, H, D] (token t, head h at t*tok_stride + h*head_stride).
 // K store: head h, key j at k_dst + h*k_hs + j*D.  V^T: (h, d, key j) at vt_dst + h*vt_hs +
-// d*vt_ds + j.  runs map launch frames to their key-space frame (slot) in dst0; nruns == 0
-// means key = token, and the V^T rows are written (zero-filled) up to row_pad keys.
-// k_src == nullptr writes V only.  vt_to_tok reads vt_dst and writes token-major rows to k_dst.
+// (j / 64)*vt_bs + d*vt_ds + j % 64 (bf16 tiles: vt_bs = 64*D, vt_ds = 64; fp32 rows:
+// vt_bs = 64, vt_ds = row length).  runs map launch frames to their key-space frame (slot) in
+// dst0, and the launch's workgroups cover the 64-key tiles of those key ranges (whole tiles
+// are written as contiguous blocks); nruns == 0 means key = token, and V^T is written
+// (zero-filled) up to row_pad keys.  k_src == nullptr writes V only.  vt_to_tok reads vt_dst
+// and writes token-major rows to k_dst.
 struct WriteArgs {
   const void* k_src;
   const void* v_src;
@@ -24,12 +27,15 @@ struct WriteArgs {
   void* k_dst;
   int64_t k_hs;
   void* vt_dst;
-  int64_t vt_hs, vt_ds;
+  int64_t vt_hs, vt_ds, vt_bs;
   FrameRun runs[3];
   int32_t nruns;
   int32_t F, H, D;
   int32_t n_tok;
   int32_t row_pad;
+  // filled by launch_write_kv for nruns > 0: run r covers 64-key tiles tile0[r] ... and the
+  // launch's workgroups [tile_pre[r], tile_pre[r + 1])
+  int32_t tile0[3], tile_pre[4];
 };
 hipError_t launch_write_kv(const WriteArgs& a, int elt, hipStream_t stream);
 

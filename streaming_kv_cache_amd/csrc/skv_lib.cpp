@@ -69,8 +69,15 @@ skv::TokView token_view(const skv::Geometry& g, const void* base) {
 
 float softmax_scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
 
-// V store: V^T[h][d][key], key = slot*F + token, rows of W*F keys.
-int64_t vt_row(const skv::Geometry& g) { return (int64_t)g.W * g.F; }
+// V store: V^T of key = slot*F + token, W*F keys per head padded to whole 64-key tiles; bf16 in
+// tiles ([h][key / 64][d][key % 64]), fp32 in rows ([h][d][key]).
+int64_t vt_row(const skv::Geometry& g) { return ((int64_t)g.W * g.F + 63) / 64 * 64; }
+// V^T strides of a buffer of `keys` keys per head (a multiple of 64) in the layout of g's dtype.
+void set_vt(skv::WriteArgs& w, const skv::Geometry& g, int64_t keys) {
+  w.vt_hs = (int64_t)g.D * keys;
+  w.vt_bs = g.dtype == SKV_BF16 ? (int64_t)skv::kVtKeys * g.D : skv::kVtKeys;
+  w.vt_ds = g.dtype == SKV_BF16 ? skv::kVtKeys : keys;
+}
 // Current-chunk V^T rows in the workspace: c*F keys padded to a multiple of 64.
 int64_t cur_row(const skv::Geometry& g) { return ((int64_t)g.c * g.F + 63) / 64 * 64; }
 // Workspace: [REL window keys, (W-c)*F*H*D (not with fused rotation)]
@@ -112,8 +119,7 @@ skv::WriteArgs stage_args(const skv_cache* c, const void* v_cur) {
   wa.tok_stride = (int64_t)g.H * g.D;
   wa.head_stride = g.D;
   wa.vt_dst = ws_vt(c);
-  wa.vt_hs = (int64_t)g.D * cur_row(g);
-  wa.vt_ds = cur_row(g);
+  set_vt(wa, g, cur_row(g));
   wa.nruns = 0;
   wa.F = g.F;
   wa.H = g.H;
@@ -208,7 +214,8 @@ skv_status kv_cache_bytes(const skv_config* cfg, size_t* store_bytes_each, size_
   skv::Geometry g;
   skv_status st = skv::make_geometry(cfg, &g);
   if (st != SKV_OK) return st;
-  *store_bytes_each = (size_t)skv::store_elems(g) * g.elt;
+  // the V store (V^T padded to whole 64-key tiles) is at least the K store's W*F*H*D elements
+  *store_bytes_each = (size_t)(g.H * g.D * vt_row(g)) * g.elt;
   *workspace_bytes = (size_t)(ws_split_off(g) + ws_split_bytes(g));
   return SKV_OK;
 }
@@ -294,8 +301,7 @@ skv_status kv_cache_append_evict(skv_cache* c, const void* k, const void* v, int
   wa.k_dst = c->k_store;
   wa.k_hs = (int64_t)g.W * g.F * g.D;
   wa.vt_dst = c->v_store;
-  wa.vt_hs = (int64_t)g.D * vt_row(g);
-  wa.vt_ds = vt_row(g);
+  set_vt(wa, g, vt_row(g));
   for (int i = 0; i < 3; ++i) wa.runs[i] = i < nruns ? runs[i] : skv::FrameRun{0, 0, 0, 0};
   wa.nruns = nruns;
   wa.F = g.F;
@@ -453,12 +459,22 @@ static skv_status attention_args(skv_cache* c, const void* q, const void* k_cur,
     }
     sg.k_rs = g.D;
     const int64_t key0 = (int64_t)r.slot0 * g.F;
-    sg.v = byte_ptr(c->v_store, key0, g.elt);
     sg.v_hs = (int64_t)g.D * vt_row(g);
     sg.v_rs = 1;
-    sg.v_ds = vt_row(g);
+    if (g.dtype == SKV_BF16) {
+      // the tile holding key0; key0 sits at position key0 % 64 of it
+      sg.v = byte_ptr(c->v_store, key0 / skv::kVtKeys * skv::kVtKeys * g.D, g.elt);
+      sg.v_phase = (int32_t)(key0 % skv::kVtKeys);
+      sg.v_ds = skv::kVtKeys;
+    } else {
+      sg.v = byte_ptr(c->v_store, key0, g.elt);
+      sg.v_phase = 0;
+      sg.v_ds = vt_row(g);
+    }
     sg.n = r.frames * g.F;
-    sg.v_al16 = (key0 % per16 == 0 && vt_row(g) % per16 == 0) ? 1 : 0;
+    // 16-byte pieces of 8 keys: the range must start and end on a piece boundary, since the last
+    // piece of a partial tile is read whole and the keys after the range may never have been written
+    sg.v_al16 = (key0 % per16 == 0 && sg.n % per16 == 0) ? 1 : 0;
     a->seg[a->nseg++] = sg;
   }
   skv::KvSeg cur;
@@ -468,11 +484,12 @@ static skv_status attention_args(skv_cache* c, const void* q, const void* k_cur,
   cur.v = ws_vt(c);
   cur.v_hs = (int64_t)g.D * cur_row(g);
   cur.v_rs = 1;
-  cur.v_ds = cur_row(g);
+  cur.v_ds = g.dtype == SKV_BF16 ? skv::kVtKeys : cur_row(g);
   cur.n = g.c * g.F;
   cur.v_al16 = 1;
+  cur.v_phase = 0;
   a->seg[a->nseg++] = cur;
-  for (int i = a->nseg; i < 4; ++i) a->seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = a->nseg; i < 4; ++i) a->seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
   return SKV_OK;
 }
 
@@ -556,7 +573,7 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
   a.nseg = 1;
   a.seg[0] = skv::KvSeg{k_text, v_text, (int64_t)head_dim, (int64_t)heads * head_dim,
                         (int64_t)head_dim, (int64_t)heads * head_dim, 1, n_text, 0};
-  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
   const hipError_t e = dtype == SKV_BF16 ? gate([&] { return skv::launch_attention_bf16_tokv(a, head_dim, (hipStream_t)stream); })
                                          : gate([&] { return skv::launch_attention_f32(a, head_dim, (hipStream_t)stream); });
   return e == hipSuccess ? SKV_OK : SKV_ERR_HIP;
@@ -624,7 +641,8 @@ skv_status text_cache_prepare(const void* k_text, const void* v_text, int32_t n_
   wa.head_stride = head_dim;
   wa.vt_dst = vdst;
   wa.vt_hs = (int64_t)head_dim * L.pad;
-  wa.vt_ds = L.pad;
+  wa.vt_bs = (int64_t)skv::kVtKeys * head_dim;
+  wa.vt_ds = skv::kVtKeys;
   wa.nruns = 0;
   wa.F = n_text;
   wa.H = heads;
@@ -656,11 +674,11 @@ skv_status cross_attention_cached(const void* q, int32_t n_q, const void* store,
   a.H = heads;
   a.sl2 = softmax_scale_log2(head_dim);
   a.nseg = 1;
-  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
   if (dtype == SKV_BF16) {
     // K token-major as given; V^T rows of L.pad keys per (head, dim)
     a.seg[0] = skv::KvSeg{store, vsrc, (int64_t)head_dim, (int64_t)heads * head_dim, (int64_t)head_dim * L.pad, 1,
-                          L.pad, n_text, 1};
+                          skv::kVtKeys, n_text, 1, 0};
     return gate([&] { return skv::launch_attention_bf16_vt(ab, head_dim, s); }) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
   }
   a.seg[0] = skv::KvSeg{store, vsrc, (int64_t)head_dim, (int64_t)heads * head_dim, (int64_t)head_dim,
@@ -712,8 +730,7 @@ skv_status block_causal_attention(const skv_config* cfg, const void* q, const vo
   wa.tok_stride = (int64_t)g.H * g.D;
   wa.head_stride = g.D;
   wa.vt_dst = workspace;
-  wa.vt_hs = (int64_t)g.D * row_pad;
-  wa.vt_ds = row_pad;
+  set_vt(wa, g, row_pad);
   wa.nruns = 0;
   wa.F = g.F;
   wa.H = g.H;
@@ -731,9 +748,9 @@ skv_status block_causal_attention(const skv_config* cfg, const void* q, const vo
   a.H = g.H;
   a.sl2 = softmax_scale_log2(g.D);
   a.nseg = 1;
-  a.seg[0] = skv::KvSeg{k, workspace, (int64_t)g.D, (int64_t)g.H * g.D, (int64_t)g.D * row_pad, 1, row_pad,
-                        n_frames * g.F, 1};
-  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0};
+  a.seg[0] = skv::KvSeg{k, workspace, (int64_t)g.D, (int64_t)g.H * g.D, (int64_t)g.D * row_pad, 1, skv::kVtKeys,
+                        n_frames * g.F, 1, 0};
+  for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
   a.mF = g.F;
   a.mq0 = q_frame0;
   a.mc = g.c;
@@ -797,8 +814,7 @@ skv_status kv_cache_gather(const skv_cache* cc, void* k_out, void* v_out, int64_
   va.tok_stride = (int64_t)g.H * g.D;
   va.head_stride = g.D;
   va.vt_dst = c->v_store;
-  va.vt_hs = (int64_t)g.D * vt_row(g);
-  va.vt_ds = vt_row(g);
+  set_vt(va, g, vt_row(g));
   for (int i = 0; i < 3; ++i)
     va.runs[i] = i < nruns ? skv::FrameRun{runs[i].start, runs[i].count, 0, runs[i].src0} : skv::FrameRun{0, 0, 0, 0};
   va.nruns = nruns;
@@ -848,8 +864,7 @@ skv_status kv_cache_restore(skv_cache* c, const void* k, const void* v, const in
     wa.k_dst = c->k_store;
     wa.k_hs = (int64_t)g.W * g.F * g.D;
     wa.vt_dst = c->v_store;
-    wa.vt_hs = (int64_t)g.D * vt_row(g);
-    wa.vt_ds = vt_row(g);
+    set_vt(wa, g, vt_row(g));
     for (int i = 0; i < 3; ++i) wa.runs[i] = i < nruns ? runs[i] : skv::FrameRun{0, 0, 0, 0};
     wa.nruns = nruns;
     wa.F = g.F;

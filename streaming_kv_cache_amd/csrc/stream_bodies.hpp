@@ -116,18 +116,19 @@ __device__ __forceinline__ void rope_block(const RopeArgs a, unsigned bx, unsign
 
 // ---------------------------------------------------------------- K rows + V^T
 // Cache write-back and current-chunk staging: token-major [tokens, H, D] in,
-// head-major K rows and transposed V (V^T[h][d][key]) out.
+// head-major K rows and transposed V out (V^T in 64-key tiles for bf16, rows for fp32).
 //
-// Each thread moves a P x P block (P = elements per 16 bytes) of one head: P
-// consecutive tokens times one 16-byte chunk of head_dim.  It issues all of its
-// loads first (K and V), writes the K pieces to their slot rows, transposes the V
-// block in registers and writes P pieces of V^T rows.  All accesses are 16 bytes
-// wide; threads are ordered so that each store instruction covers whole 128-byte
-// runs of a V^T row.
+// A write block covers 64 consecutive keys of one head: staging keys (= tokens), or one
+// 64-key tile of the key ranges the frames go to (write-back), so that a block whose keys
+// all belong to the frames writes a whole, contiguous K block (64 rows) and, in bf16, a
+// whole V^T tile.  Each thread moves a P x P block (P = elements per 16 bytes) of one head:
+// P consecutive keys times one 16-byte chunk of head_dim.  It issues all of its loads first
+// (K and V), writes the K pieces to their rows, transposes the V block in registers and
+// writes P pieces of V^T.  All accesses are 16 bytes wide.
 // [LB-fast] "3. KV 缓存 滚动窗口" / [ABot-stream] 机制二 (clean write-back of the
 // chunk's K/V); the slot of each frame comes from the ring mapping on the host
 // (FrameRun.dst0 = slot).
-constexpr int kTT = 64;   // tokens per write block
+constexpr int kTT = kVtKeys;   // keys per write block
 
 template <typename T>
 struct Per16 {
@@ -150,6 +151,12 @@ __device__ __forceinline__ int frame_dst(const WriteArgs& a, int fi) {
   return df;
 }
 
+// V^T element (h's base vh, dim d, key j).
+template <typename T>
+__device__ __forceinline__ T* vt_elem(const WriteArgs& a, T* vh, int d, int64_t j) {
+  return vh + (j / kTT) * a.vt_bs + (int64_t)d * a.vt_ds + j % kTT;
+}
+
 // Element e of each of the P 16-byte rows in, gathered into one 16-byte row: the
 // transpose of a P x P block of 16- or 32-bit elements.
 template <typename T>
@@ -169,62 +176,64 @@ __device__ __forceinline__ u32x4_t column(const u32x4_t (&in)[Per16<T>::n], int 
   return r;
 }
 
-// One write block of write_block_threads<T, D>() threads: tokens bx * 64 ... (+63) of head h
-// (or, when staging, keys bx * 64 ... of the padded V^T rows).
-// Thread tid: token group tg = tid % (64 / P) (tokens t0 + P tg ...), chunk dc = tid / (64 / P).
+// One write block of write_block_threads<T, D>() threads: 64 keys of head h, block bx.
+// Thread tid: key group tg = tid % (64 / P) (keys kb, kb + 1, ... kb + P - 1), chunk dc = tid / (64 / P).
 template <typename T, int D>
 __device__ __forceinline__ void write_kv_block(const WriteArgs a, unsigned bx, int h, unsigned tid) {
   constexpr int P = Per16<T>::n;  // elements per 16 bytes
-  constexpr int NG = kTT / P;     // token groups per block
+  constexpr int NG = kTT / P;     // key groups per block
   const int tg = tid % NG, dc = tid / NG;
-  const int tb = bx * kTT + tg * P;  // first token of this thread's block
-
-  u32x4_t kv[P], vv[P];
-  const u32x4_t z = {0u, 0u, 0u, 0u};
-  // ---- every load first
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const bool ok = tb + j < a.n_tok;
-    const int64_t off = (int64_t)(tb + j) * a.tok_stride + h * a.head_stride + dc * P;
-    kv[j] = (a.k_src && ok) ? *(const u32x4_t*)((const T*)a.k_src + off) : z;
-    vv[j] = ok ? *(const u32x4_t*)((const T*)a.v_src + off) : z;
+  // this block's keys, and the key range [klo, khi) of its frames with the token of key klo
+  int kb, klo, khi, tok0;
+  if (a.nruns == 0) {
+    // staging: key = token; keys up to row_pad (tokens past n_tok load zeros)
+    kb = (int)bx * kTT + tg * P;
+    klo = 0;
+    khi = a.row_pad;
+    tok0 = 0;
+  } else {
+    int r = 0;
+    while (r + 1 < a.nruns && (int)bx >= a.tile_pre[r + 1]) ++r;
+    kb = (a.tile0[r] + ((int)bx - a.tile_pre[r])) * kTT + tg * P;
+    klo = a.runs[r].dst0 * a.F;
+    khi = klo + a.runs[r].count * a.F;
+    tok0 = a.runs[r].start * a.F;
   }
-  // ---- K pieces -> head-major store rows (frame slot * F + token)
-  if (a.k_src) {
+  if (kb + P <= klo || kb >= khi) return;  // none of this thread's keys are written here
+  T* vh = (T*)a.vt_dst + h * a.vt_hs;
+  T* kh = a.k_src ? (T*)a.k_dst + h * a.k_hs : nullptr;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  if (kb >= klo && kb + P <= khi) {
+    // P whole keys: tokens tb .. tb + P - 1
+    const int tb = kb - klo + tok0;
+    u32x4_t kv[P], vv[P];
+    // ---- every load first
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-      const int gt = tb + j;
-      if (gt < a.n_tok) {
-        const int fi = gt / a.F, tok = gt - fi * a.F;
-        const int64_t key = (int64_t)frame_dst(a, fi) * a.F + tok;
-        *(u32x4_t*)((T*)a.k_dst + h * a.k_hs + key * D + dc * P) = kv[j];
-      }
+      const bool ok = tb + j < a.n_tok;
+      const int64_t off = (int64_t)(tb + j) * a.tok_stride + h * a.head_stride + dc * P;
+      kv[j] = (kh && ok) ? *(const u32x4_t*)((const T*)a.k_src + off) : z;
+      vv[j] = ok ? *(const u32x4_t*)((const T*)a.v_src + off) : z;
     }
-  }
-  // ---- V: P rows of V^T (d = dc * P + e), keys tb .. tb + P - 1
-  T* vh = (T*)a.vt_dst + h * a.vt_hs;
-  if (a.nruns == 0) {
-    // staging: key = token; the row tail up to row_pad is written with the zeros loaded for it
-    if (tb < a.row_pad) {
+    // ---- K pieces -> key rows
+    if (kh) {
 #pragma unroll
-      for (int e = 0; e < P; ++e) *(u32x4_t*)(vh + (int64_t)(dc * P + e) * a.vt_ds + tb) = column<T>(vv, e);
+      for (int j = 0; j < P; ++j) *(u32x4_t*)(kh + (int64_t)(kb + j) * D + dc * P) = kv[j];
     }
-  } else if (tb < a.n_tok) {
-    const int fi = tb / a.F, tok = tb - fi * a.F;
-    const int64_t k0 = (int64_t)frame_dst(a, fi) * a.F + tok;
-    const bool whole = tb + P <= a.n_tok && tok + P <= a.F && (k0 % P) == 0 && (a.vt_ds % P) == 0 &&
-                       ((uintptr_t)vh & 15) == 0;
-    if (whole) {
+    // ---- V: P pieces of V^T (d = dc * P + e), keys kb .. kb + P - 1 (one 16-byte run: kb % P == 0)
 #pragma unroll
-      for (int e = 0; e < P; ++e) *(u32x4_t*)(vh + (int64_t)(dc * P + e) * a.vt_ds + k0) = column<T>(vv, e);
-    } else {
-      for (int j = 0; j < P && tb + j < a.n_tok; ++j) {
-        const int gt = tb + j, f2 = gt / a.F;
-        const int64_t key = (int64_t)frame_dst(a, f2) * a.F + (gt - f2 * a.F);
-        const T* src = (const T*)&vv[j];
+    for (int e = 0; e < P; ++e) *(u32x4_t*)vt_elem<T>(a, vh, dc * P + e, kb) = column<T>(vv, e);
+  } else {
+    // a group cut by the frames' bounds (frames whose token count is not a multiple of P): key by key
+    for (int j = 0; j < P; ++j) {
+      const int key = kb + j;
+      if (key < klo || key >= khi) continue;
+      const int64_t off = (int64_t)(key - klo + tok0) * a.tok_stride + h * a.head_stride + dc * P;
+      if (kh) *(u32x4_t*)(kh + (int64_t)key * D + dc * P) = *(const u32x4_t*)((const T*)a.k_src + off);
+      const u32x4_t v1 = *(const u32x4_t*)((const T*)a.v_src + off);
+      const T* src = (const T*)&v1;
 #pragma unroll
-        for (int e = 0; e < P; ++e) vh[(int64_t)(dc * P + e) * a.vt_ds + key] = src[e];
-      }
+      for (int e = 0; e < P; ++e) *vt_elem<T>(a, vh, dc * P + e, key) = src[e];
     }
   }
 }

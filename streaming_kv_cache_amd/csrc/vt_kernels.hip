@@ -13,7 +13,7 @@ constexpr int kThreads = 256;  // threads of the gather kernel
 
 }  // namespace
 
-// grid = (ceil(n_tok / 64) [or row_pad / 64 for staging], H); block = write_block_threads<T, D>().
+// grid = (64-key tiles of the runs' keys [or row_pad / 64 for staging], H); block = write_block_threads<T, D>().
 template <typename T, int D>
 __global__ __launch_bounds__((write_block_threads<T, D>())) void write_kv_kernel(WriteArgs a) {
   write_kv_block<T, D>(a, blockIdx.x, blockIdx.y, threadIdx.x);
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void vt_to_tok_kernel(WriteArgs a) {
     const int gt = t0 + t;
     if (gt < a.n_tok) {
       const int fi = gt / a.F;
-      tile[t][d] = src[(int64_t)d * a.vt_ds + (int64_t)frame_dst(a, fi) * a.F + (gt - fi * a.F)];
+      tile[t][d] = *vt_elem<const T>(a, src, d, (int64_t)frame_dst(a, fi) * a.F + (gt - fi * a.F));
     }
   }
   __syncthreads();
@@ -59,9 +59,25 @@ static hipError_t launch_write_t(const WriteArgs& a, dim3 grid, hipStream_t stre
   return hipGetLastError();
 }
 
-hipError_t launch_write_kv(const WriteArgs& a, int elt, hipStream_t stream) {
-  dim3 grid((a.n_tok + kTT - 1) / kTT, a.H);
-  if (a.nruns == 0) grid.x = (a.row_pad + kTT - 1) / kTT;
+hipError_t launch_write_kv(const WriteArgs& in, int elt, hipStream_t stream) {
+  WriteArgs a = in;
+  dim3 grid((a.row_pad + kTT - 1) / kTT, a.H);
+  if (a.nruns > 0) {
+    // one workgroup per 64-key tile touched by each run's keys [dst0 * F, (dst0 + count) * F)
+    int total = 0;
+    for (int r = 0; r < 3; ++r) {
+      a.tile_pre[r] = total;
+      a.tile0[r] = 0;
+      if (r < a.nruns && a.runs[r].count > 0) {
+        const int64_t lo = (int64_t)a.runs[r].dst0 * a.F, hi = lo + (int64_t)a.runs[r].count * a.F;
+        a.tile0[r] = (int)(lo / kTT);
+        total += (int)((hi - 1) / kTT - lo / kTT + 1);
+      }
+    }
+    a.tile_pre[3] = total;
+    grid.x = total;
+  }
+  if (grid.x == 0) return hipSuccess;
   return elt == 2 ? launch_write_t<uint16_t>(a, grid, stream) : launch_write_t<uint32_t>(a, grid, stream);
 }
 

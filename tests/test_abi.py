@@ -42,11 +42,12 @@ def test_cache_bytes():
     # workspace = REL window keys [(W-c)*F, H, D] + current-chunk V^T [H, D, c*F rounded up to 64]
     def pad64(n):
         return (n + 63) // 64 * 64
+    # one size serves both stores: the V store's V^T, W*F keys per head padded to 64-key tiles
     store, ws = skv.cache_bytes(ABOT)
-    assert store == 21 * 880 * 24 * 128 * 2
+    assert store == pad64(21 * 880) * 24 * 128 * 2
     assert ws == (21 - 3) * 880 * 24 * 128 * 2 + 24 * 128 * pad64(3 * 880) * 2
     store, ws = skv.cache_bytes(LB480)
-    assert store == 18 * 1560 * 40 * 128 * 2 and ws == 40 * 128 * pad64(4 * 1560) * 2
+    assert store == pad64(18 * 1560) * 40 * 128 * 2 and ws == 40 * 128 * pad64(4 * 1560) * 2
     tiny = skv.Config(2, 64, 4, 4, 2, 1, 4, dtype=skv.F32)
     assert skv.cache_bytes(tiny) == (4 * 16 * 2 * 64 * 4, 2 * 64 * 64 * 4)
     # 3 heads of 480P: 49 query tiles x 3 heads = 147 four-wave workgroups fill less than half of

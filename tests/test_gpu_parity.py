@@ -386,8 +386,9 @@ def test_cross_attention_cached(dtype, n_q, n_text, h, d, waves, monkeypatch):
 
 @pytest.mark.parametrize("dtype,n_text,h,d", [(skv.BF16, 77, 3, 64), (skv.BF16, 512, 4, 128), (skv.F32, 9, 2, 32)])
 def test_text_cache_layout(dtype, n_text, h, d):
-    """The prepared store holds the bytes the header states: the K copy, then (bf16) V^T rows of
-    roundup(n_text, 64) keys with zero padding, (fp32) the V copy, at the next 256-byte boundary."""
+    """The prepared store holds the bytes the header states: the K copy, then (bf16) V^T in tiles of
+    64 keys ([h][key / 64][d][key % 64], keys past n_text zero), (fp32) the V copy, at the next
+    256-byte boundary."""
     say(f"[text store] dtype={dtype} n_text={n_text} h={h} d={d}")
     tdt = torch.bfloat16 if dtype == skv.BF16 else torch.float32
     kt = si.draw((n_text, h, d), 0, 0, 1, si.TEXT_K, tdt).cuda()
@@ -400,7 +401,8 @@ def test_text_cache_layout(dtype, n_text, h, d):
     assert torch.equal(store[:kb].view(tdt).view(n_text, h, d), kt)
     if dtype == skv.BF16:
         pad = (n_text + 63) // 64 * 64
-        v_t = store[off:].view(tdt).view(h, d, pad)
+        tiles = store[off:].view(tdt).view(h, pad // 64, d, 64)
+        v_t = tiles.permute(0, 2, 1, 3).reshape(h, d, pad)      # back to [h][d][key]
         assert torch.equal(v_t[:, :, :n_text], vt.permute(1, 2, 0))
         assert not v_t[:, :, n_text:].any()
     else:
