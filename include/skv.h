@@ -240,12 +240,12 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
  * its note on the cross-attention cache; [ABot-stream] "一次流式生成的完整链路",
  * step 1: the 512-token text cache is built once, and a prompt change rebuilds
  * only it), so their layout is fixed once:
- * text_cache_prepare copies k_text and stores v_text transposed (the keys padded
- * to a multiple of 64 with zeros) into `store`, a caller-allocated
- * device buffer of text_cache_bytes(...) bytes, 256-byte aligned.  bf16: the
- * copy of k_text [n_text, H, D] is followed, at the next 256-byte boundary, by
- * V^T in tiles of 64 keys, [H][P/64][D][64] with P = roundup(n_text, 64) and the
- * keys past n_text zero; fp32: copies of k_text and v_text back to back.
+ * text_cache_prepare lays k_text and v_text out into `store`, a caller-allocated
+ * device buffer of text_cache_bytes(...) bytes, 256-byte aligned.  bf16, with
+ * P = roundup(n_text, 64) and the keys past n_text zero: K head-major [H][P][D]
+ * (one head's keys contiguous, as in the K store), then, at the next 256-byte
+ * boundary, V^T in tiles of 64 keys, [H][P/64][D][64]; fp32: copies of k_text
+ * and v_text ([n_text, H, D]) back to back, the second at a 256-byte boundary.
  * cross_attention_cached then attends q/out [n_q, H, D] over the store with the
  * same result definition as cross_attention (bf16: the matrix-core kernel of
  * chunk_attention, which reads V^T with direct-to-LDS loads).  The store is

@@ -1036,17 +1036,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_vt_kernel(
     }
     return;
   }
+  // Normalise, then write whole output rows: a lane holds O^T[d][query l32] for d = 32 mb + 8 g +
+  // 4 hf + 0..3, so written directly every store instruction would touch 16 bytes of 32 rows.  The
+  // wave's 32 rows go through its own part of the (now idle) tile stages instead and leave as
+  // 16-byte pieces of consecutive bytes (4 or 8 whole rows per instruction).
   const float inv = 1.f / l_row;
-  if (qi < a.Lq) {
-    uint16_t* op = (uint16_t*)a.out + ((int64_t)qi * a.H + h) * D + 4 * hf;
+  constexpr int OP = 2 * D + 16;  // LDS pitch of an output row: data + a 16-byte pad
+  static_assert(NW * 32 * OP <= NSTAGE * (KT_B + VT_B), "output rows fit the tile stages");
+  __syncthreads();  // every wave is done with the stages
+  uint8_t* ob_lds = smem + wave * 32 * OP;
 #pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb)
+  for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2_t w = {pack_bf16x2(o[mb][4 * g] * inv, o[mb][4 * g + 1] * inv),
-                           pack_bf16x2(o[mb][4 * g + 2] * inv, o[mb][4 * g + 3] * inv)};
-        *(u32x2_t*)(op + 32 * mb + 8 * g) = w;
-      }
+    for (int g = 0; g < 4; ++g) {
+      const u32x2_t w = {pack_bf16x2(o[mb][4 * g] * inv, o[mb][4 * g + 1] * inv),
+                         pack_bf16x2(o[mb][4 * g + 2] * inv, o[mb][4 * g + 3] * inv)};
+      *(u32x2_t*)(ob_lds + l32 * OP + 2 * (32 * mb + 8 * g + 4 * hf)) = w;
+    }
+  constexpr int CPR = 2 * D / 16;   // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR;     // rows per instruction
+#pragma unroll
+  for (int j = 0; j < 32 / RPI; ++j) {
+    const int r = RPI * j + lane / CPR, c = lane % CPR;
+    const u32x4_t v = *(const u32x4_t*)(ob_lds + r * OP + 16 * c);
+    if (q_base + r < a.Lq) *(u32x4_t*)((uint8_t*)a.out + ((int64_t)(q_base + r) * a.H + h) * (2 * D) + 16 * c) = v;
   }
 }
 

@@ -579,7 +579,8 @@ skv_status cross_attention(const void* q, int32_t n_q, const void* k_text, const
   return e == hipSuccess ? SKV_OK : SKV_ERR_HIP;
 }
 
-// Prepared text cache: [copy of k_text, n_text*H*D] [256-byte boundary] [bf16: V^T, H*D*pad | fp32: v_text copy].
+// Prepared text cache: bf16 [K head-major, H*pad*D] [256-byte boundary] [V^T tiles, H*D*pad];
+// fp32 [copy of k_text, n_text*H*D] [256-byte boundary] [copy of v_text].
 struct TextLayout {
   int64_t k_bytes = 0, vt_off = 0, total = 0, pad = 0;
 };
@@ -589,14 +590,13 @@ static skv_status text_layout(int32_t n_text, int32_t heads, int32_t head_dim, i
   if (!skv::attention_head_dim_supported(dtype, head_dim)) return SKV_ERR_CONFIG;
   if (n_text < 1 || n_text > (1 << 30)) return SKV_ERR_SHAPE;
   const int64_t elt = dtype == SKV_BF16 ? 2 : 4;
-  L->k_bytes = (int64_t)n_text * heads * head_dim * elt;
   L->pad = ((int64_t)n_text + 63) / 64 * 64;
+  // bf16: one head's keys are contiguous rows (as in the K store), padded with zero rows
+  L->k_bytes = dtype == SKV_BF16 ? (int64_t)heads * L->pad * head_dim * 2 : (int64_t)n_text * heads * head_dim * elt;
   L->vt_off = (L->k_bytes + 255) / 256 * 256;
   if (dtype == SKV_BF16) {
-    // the matrix-core kernel addresses one head's keys with 32-bit byte offsets: token-major K rows
-    // (H*D apart, plus one tile of slack) and V^T rows of pad keys
-    if (((int64_t)n_text + 64) * heads * head_dim * 2 > INT32_MAX || (int64_t)head_dim * L->pad * 2 > INT32_MAX)
-      return SKV_ERR_SHAPE;
+    // the matrix-core kernel addresses one head's keys and V^T with 32-bit byte offsets
+    if ((int64_t)head_dim * L->pad * 2 > INT32_MAX) return SKV_ERR_SHAPE;
     L->total = L->vt_off + (int64_t)heads * head_dim * L->pad * 2;
   } else {
     L->total = L->vt_off + L->k_bytes;
@@ -627,15 +627,22 @@ skv_status text_cache_prepare(const void* k_text, const void* v_text, int32_t n_
   TextLayout L;
   if ((st = text_layout(n_text, heads, head_dim, dtype, &L)) != SKV_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
-  if (gate([&] { return hipMemcpyAsync(store, k_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s); }) != hipSuccess)
-    return SKV_ERR_HIP;
   char* vdst = (char*)store + L.vt_off;
-  if (dtype != SKV_BF16)
-    return gate([&] { return hipMemcpyAsync(vdst, v_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s); }) == hipSuccess ? SKV_OK
-                                                                                                 : SKV_ERR_HIP;
-  // values -> V^T rows [h][d][key], keys past n_text zero up to the padded row length
+  if (dtype != SKV_BF16) {
+    if (gate([&] { return hipMemcpyAsync(store, k_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s); }) !=
+        hipSuccess)
+      return SKV_ERR_HIP;
+    return gate([&] { return hipMemcpyAsync(vdst, v_text, (size_t)L.k_bytes, hipMemcpyDeviceToDevice, s); }) ==
+                   hipSuccess
+               ? SKV_OK
+               : SKV_ERR_HIP;
+  }
+  // one launch: keys -> head-major rows [h][key][d], values -> V^T tiles; keys past n_text zero
+  // up to the padded length
   skv::WriteArgs wa{};
-  wa.k_src = nullptr;
+  wa.k_src = k_text;
+  wa.k_dst = store;
+  wa.k_hs = L.pad * head_dim;
   wa.v_src = v_text;
   wa.tok_stride = (int64_t)heads * head_dim;
   wa.head_stride = head_dim;
@@ -676,8 +683,8 @@ skv_status cross_attention_cached(const void* q, int32_t n_q, const void* store,
   a.nseg = 1;
   for (int i = 1; i < 4; ++i) a.seg[i] = skv::KvSeg{nullptr, nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
   if (dtype == SKV_BF16) {
-    // K token-major as given; V^T rows of L.pad keys per (head, dim)
-    a.seg[0] = skv::KvSeg{store, vsrc, (int64_t)head_dim, (int64_t)heads * head_dim, (int64_t)head_dim * L.pad, 1,
+    // K head-major rows of L.pad keys per head; V^T tiles of L.pad keys per head
+    a.seg[0] = skv::KvSeg{store, vsrc, L.pad * head_dim, (int64_t)head_dim, (int64_t)head_dim * L.pad, 1,
                           skv::kVtKeys, n_text, 1, 0};
     return gate([&] { return skv::launch_attention_bf16_vt(ab, head_dim, s); }) == hipSuccess ? SKV_OK : SKV_ERR_HIP;
   }

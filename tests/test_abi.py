@@ -149,9 +149,9 @@ def test_cross_attention_validation():
 def test_text_cache_sizes_and_validation():
     """Store size formula, and every error path of the prepared text cache returns before anything is
     enqueued (no GPU needed)."""
-    # bf16: K copy (512 x 40 x 128 x 2) then V^T rows padded to 64 keys, at a 256-byte boundary
+    # bf16: K head-major and V^T, each over the keys padded to a multiple of 64, V^T at a 256-byte boundary
     assert skv.text_cache_bytes(512, 40, 128, skv.BF16) == 2 * 512 * 40 * 128 * 2
-    assert skv.text_cache_bytes(77, 3, 64, skv.BF16) == (77 * 3 * 64 * 2 + 255) // 256 * 256 + 3 * 64 * 128 * 2
+    assert skv.text_cache_bytes(77, 3, 64, skv.BF16) == 3 * 128 * 64 * 2 + 3 * 64 * 128 * 2
     assert skv.text_cache_bytes(77, 3, 64, skv.F32) == (77 * 3 * 64 * 4 + 255) // 256 * 256 + 77 * 3 * 64 * 4
     b = ctypes.c_size_t()
     f = skv.lib.text_cache_bytes
@@ -160,7 +160,7 @@ def test_text_cache_sizes_and_validation():
     assert f(512, 40, 32, skv.F32, ctypes.byref(b)) == skv.OK
     assert f(0, 40, 128, skv.BF16, ctypes.byref(b)) == skv.ERR_SHAPE
     assert f(512, 0, 128, skv.BF16, ctypes.byref(b)) == skv.ERR_CONFIG
-    assert f(1 << 22, 40, 128, skv.BF16, ctypes.byref(b)) == skv.ERR_SHAPE   # past 32-bit offsets per head
+    assert f((1 << 23) + 1, 40, 128, skv.BF16, ctypes.byref(b)) == skv.ERR_SHAPE   # past 32-bit offsets per head
     p, p16, nul = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x40010), ctypes.c_void_p(0)
     g = skv.lib.text_cache_prepare
     assert g(nul, p, 512, 40, 128, skv.BF16, p, nul) == skv.ERR_NULL

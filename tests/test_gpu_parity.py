@@ -386,21 +386,26 @@ def test_cross_attention_cached(dtype, n_q, n_text, h, d, waves, monkeypatch):
 
 @pytest.mark.parametrize("dtype,n_text,h,d", [(skv.BF16, 77, 3, 64), (skv.BF16, 512, 4, 128), (skv.F32, 9, 2, 32)])
 def test_text_cache_layout(dtype, n_text, h, d):
-    """The prepared store holds the bytes the header states: the K copy, then (bf16) V^T in tiles of
-    64 keys ([h][key / 64][d][key % 64], keys past n_text zero), (fp32) the V copy, at the next
-    256-byte boundary."""
+    """The prepared store holds the bytes the header states.  bf16: K head-major ([h][key][d], rows up
+    to roundup(n_text, 64), past n_text zero), then V^T in tiles of 64 keys ([h][key / 64][d][key % 64],
+    keys past n_text zero); fp32: copies of K and V.  The second part starts at a 256-byte boundary."""
     say(f"[text store] dtype={dtype} n_text={n_text} h={h} d={d}")
     tdt = torch.bfloat16 if dtype == skv.BF16 else torch.float32
     kt = si.draw((n_text, h, d), 0, 0, 1, si.TEXT_K, tdt).cuda()
     vt = si.draw((n_text, h, d), 0, 0, 1, si.TEXT_V, tdt).cuda()
     store = skv.text_cache_prepare(kt, vt)
     torch.cuda.synchronize()
-    kb = kt.numel() * kt.element_size()
+    pad = (n_text + 63) // 64 * 64
+    kb = (h * pad * d if dtype == skv.BF16 else n_text * h * d) * kt.element_size()
     off = (kb + 255) // 256 * 256
     assert store.numel() == skv.text_cache_bytes(n_text, h, d, dtype)
-    assert torch.equal(store[:kb].view(tdt).view(n_text, h, d), kt)
     if dtype == skv.BF16:
-        pad = (n_text + 63) // 64 * 64
+        k_hm = store[:kb].view(tdt).view(h, pad, d)
+        assert torch.equal(k_hm[:, :n_text], kt.permute(1, 0, 2))
+        assert not k_hm[:, n_text:].any()
+    else:
+        assert torch.equal(store[:kb].view(tdt).view(n_text, h, d), kt)
+    if dtype == skv.BF16:
         tiles = store[off:].view(tdt).view(h, pad // 64, d, 64)
         v_t = tiles.permute(0, 2, 1, 3).reshape(h, d, pad)      # back to [h][d][key]
         assert torch.equal(v_t[:, :, :n_text], vt.permute(1, 2, 0))
