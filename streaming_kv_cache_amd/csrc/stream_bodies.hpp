@@ -90,12 +90,16 @@ __device__ __forceinline__ void rope_block(const RopeArgs a, unsigned bx, unsign
     }
   }
   const RopeJob& j = a.jobs[bz];
+  // the pair frequencies are loaded first, so that the angles wait only for them; the head loads
+  // are unconditional (heads past the group's last load that one again) so none waits for another
+  double om[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) om[p] = a.omega[g * 4 + p];
   const T* s = (const T*)j.src.base + (int64_t)(sf * a.F + tok) * j.src.tok_stride + g * 8 + h0 * j.src.head_stride;
   T* d = (T*)j.dst.base + (int64_t)(df * a.F + tok) * j.dst.tok_stride + g * 8 + h0 * j.dst.head_stride;
   typename IO::V x[kRopeHeads];
 #pragma unroll
-  for (int i = 0; i < kRopeHeads; ++i)
-    if (i < nh) x[i] = IO::load(s + i * j.src.head_stride);
+  for (int i = 0; i < kRopeHeads; ++i) x[i] = IO::load(s + (i < nh ? i : nh - 1) * j.src.head_stride);
   int64_t t = j.t0 + fi;
   if (j.clamp_max >= 0) t = t < 0 ? 0 : (t > j.clamp_max ? j.clamp_max : t);
   const int row = tok / a.gw, col = tok - row * a.gw;
@@ -105,7 +109,7 @@ __device__ __forceinline__ void rope_block(const RopeArgs a, unsigned bx, unsign
   for (int p = 0; p < 4; ++p) {
     const int pair = g * 4 + p;
     const double pos = pair < a.pair_h ? (double)t : (pair < a.pair_w ? (double)row : (double)col);
-    const double ang = pos * a.omega[pair];
+    const double ang = pos * om[p];
     const double red = ang - two_pi * rint(ang / two_pi);  // |red| <= pi
     sincosf((float)red, &sn[p], &cs[p]);
   }
@@ -178,49 +182,74 @@ __device__ __forceinline__ u32x4_t column(const u32x4_t (&in)[Per16<T>::n], int 
 
 // One write block of write_block_threads<T, D>() threads: 64 keys of head h, block bx.
 // Thread tid: key group tg = tid % (64 / P) (keys kb, kb + 1, ... kb + P - 1), chunk dc = tid / (64 / P).
-template <typename T, int D>
-__device__ __forceinline__ void write_kv_block(const WriteArgs a, unsigned bx, int h, unsigned tid) {
+// HAS_K: K rows are written too (else V only).  The common path is straight-line: every load
+// (K, then V) is unconditional and issued before the first store, K rows are stored before the
+// V^T pieces, so each group of stores waits only for its own loads.  A load under a lane
+// condition, or a value merged across a branch, makes the compiler wait for loads (and for the
+// stores issued before them) in between.
+template <typename T, int D, bool HAS_K>
+__device__ __forceinline__ void write_kv_block_impl(const WriteArgs& a, unsigned bx, int h, unsigned tid) {
   constexpr int P = Per16<T>::n;  // elements per 16 bytes
   constexpr int NG = kTT / P;     // key groups per block
   const int tg = tid % NG, dc = tid / NG;
   // this block's keys, and the key range [klo, khi) of its frames with the token of key klo
   int kb, klo, khi, tok0;
   if (a.nruns == 0) {
-    // staging: key = token; keys up to row_pad (tokens past n_tok load zeros)
+    // staging: key = token; keys up to row_pad (tokens past n_tok are written as zeros)
     kb = (int)bx * kTT + tg * P;
     klo = 0;
     khi = a.row_pad;
     tok0 = 0;
   } else {
-    int r = 0;
-    while (r + 1 < a.nruns && (int)bx >= a.tile_pre[r + 1]) ++r;
-    kb = (a.tile0[r] + ((int)bx - a.tile_pre[r])) * kTT + tg * P;
-    klo = a.runs[r].dst0 * a.F;
-    khi = klo + a.runs[r].count * a.F;
-    tok0 = a.runs[r].start * a.F;
+    // the run this block's tile belongs to (unrolled: no dynamic index into the arguments)
+    int t0 = a.tile0[0], tp = a.tile_pre[0];
+    FrameRun run = a.runs[0];
+#pragma unroll
+    for (int i = 1; i < 3; ++i)
+      if (i < a.nruns && (int)bx >= a.tile_pre[i]) {
+        t0 = a.tile0[i];
+        tp = a.tile_pre[i];
+        run = a.runs[i];
+      }
+    kb = (t0 + ((int)bx - tp)) * kTT + tg * P;
+    klo = run.dst0 * a.F;
+    khi = klo + run.count * a.F;
+    tok0 = run.start * a.F;
   }
-  if (kb + P <= klo || kb >= khi) return;  // none of this thread's keys are written here
+  if (kb + P <= klo || kb >= khi || a.n_tok <= 0) return;  // none of this thread's keys are written here
   T* vh = (T*)a.vt_dst + h * a.vt_hs;
-  T* kh = a.k_src ? (T*)a.k_dst + h * a.k_hs : nullptr;
-  const u32x4_t z = {0u, 0u, 0u, 0u};
+  T* kh = HAS_K ? (T*)a.k_dst + h * a.k_hs : nullptr;
   if (kb >= klo && kb + P <= khi) {
-    // P whole keys: tokens tb .. tb + P - 1
-    const int tb = kb - klo + tok0;
+    // P whole keys: tokens tb .. tb + P - 1; those past the last token (a staging block's padded
+    // tail) load the last token and are zeroed by their mask
+    const int tb = kb - klo + tok0, tl = a.n_tok - 1;
+    const T* ks = HAS_K ? (const T*)a.k_src + h * a.head_stride + dc * P : nullptr;
+    const T* vs = (const T*)a.v_src + h * a.head_stride + dc * P;
     u32x4_t kv[P], vv[P];
-    // ---- every load first
+    if constexpr (HAS_K) {
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const bool ok = tb + j < a.n_tok;
-      const int64_t off = (int64_t)(tb + j) * a.tok_stride + h * a.head_stride + dc * P;
-      kv[j] = (kh && ok) ? *(const u32x4_t*)((const T*)a.k_src + off) : z;
-      vv[j] = ok ? *(const u32x4_t*)((const T*)a.v_src + off) : z;
+      for (int j = 0; j < P; ++j) kv[j] = *(const u32x4_t*)(ks + (int64_t)(tb + j < tl ? tb + j : tl) * a.tok_stride);
     }
-    // ---- K pieces -> key rows
-    if (kh) {
 #pragma unroll
-      for (int j = 0; j < P; ++j) *(u32x4_t*)(kh + (int64_t)(kb + j) * D + dc * P) = kv[j];
+    for (int j = 0; j < P; ++j) vv[j] = *(const u32x4_t*)(vs + (int64_t)(tb + j < tl ? tb + j : tl) * a.tok_stride);
+    uint32_t m[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) m[j] = tb + j <= tl ? 0xffffffffu : 0u;
+    if constexpr (HAS_K) {
+      // ---- K pieces -> key rows
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        u32x4_t x = kv[j];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] &= m[j];
+        *(u32x4_t*)(kh + (int64_t)(kb + j) * D + dc * P) = x;
+      }
     }
     // ---- V: P pieces of V^T (d = dc * P + e), keys kb .. kb + P - 1 (one 16-byte run: kb % P == 0)
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vv[j][c] &= m[j];
 #pragma unroll
     for (int e = 0; e < P; ++e) *(u32x4_t*)vt_elem<T>(a, vh, dc * P + e, kb) = column<T>(vv, e);
   } else {
@@ -229,13 +258,21 @@ __device__ __forceinline__ void write_kv_block(const WriteArgs a, unsigned bx, i
       const int key = kb + j;
       if (key < klo || key >= khi) continue;
       const int64_t off = (int64_t)(key - klo + tok0) * a.tok_stride + h * a.head_stride + dc * P;
-      if (kh) *(u32x4_t*)(kh + (int64_t)key * D + dc * P) = *(const u32x4_t*)((const T*)a.k_src + off);
+      if (HAS_K) *(u32x4_t*)(kh + (int64_t)key * D + dc * P) = *(const u32x4_t*)((const T*)a.k_src + off);
       const u32x4_t v1 = *(const u32x4_t*)((const T*)a.v_src + off);
       const T* src = (const T*)&v1;
 #pragma unroll
       for (int e = 0; e < P; ++e) *vt_elem<T>(a, vh, dc * P + e, key) = src[e];
     }
   }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void write_kv_block(const WriteArgs a, unsigned bx, int h, unsigned tid) {
+  if (a.k_src)
+    write_kv_block_impl<T, D, true>(a, bx, h, tid);
+  else
+    write_kv_block_impl<T, D, false>(a, bx, h, tid);
 }
 
 }  // namespace skv
