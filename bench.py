@@ -428,6 +428,41 @@ def hbm_leg(runner, reps=10):
     us = timed(lambda: cache.append_evict(kk, v))
     res["append"] = {"avg_us": round(us, 2), "GB/s": round(4 * tensor / us / 1e3, 1),
                      "frac_hbm": round(4 * tensor / us / 1e3 / HBM_PEAK_GBS, 4)}
+    # the append's schedule position: each launch right after an attention pass (which streams the
+    # whole cache through L2 and the memory-side cache) and from sources that pass did not read;
+    # the append and a plain copy of the same bytes, timed the same way (events around the launch)
+    def attend():
+        # the pass as the schedule runs it (window re-rotation after an append, rotation and staging)
+        if runner.fused:
+            cache.chunk_attention(q, k, v, out=runner.out)
+            return
+        if runner.rel:
+            cache.rope_apply_window()
+        cache.prepare_pass(q, k, v, q_out=runner.qr, k_out=runner.kr[0], start_frame=cache.info().n_appended)
+        cache.chunk_attention(runner.qr, runner.kr[0], None, out=runner.out)
+    srcs = [torch.empty(2 * tensor, dtype=torch.uint8, device=k.device) for _ in range(4)]
+    dst = torch.empty_like(srcs[0])
+
+    def after_attention(fn):
+        xs = []
+        for i in range(reps + 1):
+            attend()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            if i:
+                xs.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(xs))
+    ua = after_attention(lambda i: cache.append_evict(k if runner.rel or runner.fused else runner.kr[0], v))
+    uc = after_attention(lambda i: dst.copy_(srcs[i % len(srcs)]))
+    res["after_attention"] = {
+        "append_us": round(ua, 2), "append_frac_hbm": round(4 * tensor / ua / 1e3 / HBM_PEAK_GBS, 4),
+        "plain_copy_us": round(uc, 2), "plain_copy_frac_hbm": round(4 * tensor / uc / 1e3 / HBM_PEAK_GBS, 4),
+        "note": "one launch right after an attention pass, sources not read by it; median of "
+                f"{reps} launches, events around the launch (includes its dispatch)"}
+    del srcs, dst
     us = timed(lambda: cache.stage_v(v))
     res["stage_v"] = {"avg_us": round(us, 2), "GB/s": round(2 * tensor / us / 1e3, 1)}
     if not runner.fused:

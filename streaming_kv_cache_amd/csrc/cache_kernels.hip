@@ -142,12 +142,13 @@ __global__ __launch_bounds__(kRopeThreads) void prepare_pass_kernel(RopeArgs r, 
     static_assert(kRopeThreads % WT == 0, "staging blocks must tile the workgroup");
     const int sb = (b - n_rope) * (kRopeThreads / WT) + (int)threadIdx.x / WT;
     if (sb >= n_stage) return;
-    write_kv_block<uint16_t, D>(w, sb % stage_gx, sb / stage_gx, (int)threadIdx.x % WT);
+    write_kv_block<uint16_t, D, false>(w, sb % stage_gx, sb / stage_gx, (int)threadIdx.x % WT);
   }
 }
 
 hipError_t launch_prepare_pass(const RopeLaunch& L, const WriteArgs& w, hipStream_t stream) {
-  if (L.njobs < 1 || L.njobs > 3 || !L.dtype_bf16 || w.nruns != 0 || L.D != w.D) return hipErrorInvalidValue;
+  // the staging half writes V^T only (the rotary half writes k)
+  if (L.njobs < 1 || L.njobs > 3 || !L.dtype_bf16 || w.nruns != 0 || w.k_src || L.D != w.D) return hipErrorInvalidValue;
   dim3 rg;
   const RopeArgs r = rope_args(L, &rg);
   const int n_rope = (int)(rg.x * rg.y * rg.z);

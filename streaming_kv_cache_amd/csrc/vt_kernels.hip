@@ -14,9 +14,11 @@ constexpr int kThreads = 256;  // threads of the gather kernel
 }  // namespace
 
 // grid = (64-key tiles of the runs' keys [or row_pad / 64 for staging], H); block = write_block_threads<T, D>().
-template <typename T, int D>
+// HAS_K: K rows too (one instantiation each, so that the V-only one keeps its smaller register
+// budget and occupancy).
+template <typename T, int D, bool HAS_K>
 __global__ __launch_bounds__((write_block_threads<T, D>())) void write_kv_kernel(WriteArgs a) {
-  write_kv_block<T, D>(a, blockIdx.x, blockIdx.y, threadIdx.x);
+  write_kv_block<T, D, HAS_K>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // V^T -> token-major (logical gather, not on the hot path).  grid = (ceil(n_tok / 64), H);
@@ -47,13 +49,13 @@ __global__ __launch_bounds__(kThreads) void vt_to_tok_kernel(WriteArgs a) {
   }
 }
 
-template <typename T>
+template <typename T, bool HAS_K>
 static hipError_t launch_write_t(const WriteArgs& a, dim3 grid, hipStream_t stream) {
   constexpr int P = Per16<T>::n;
   switch (a.D) {
-    case 32: hipLaunchKernelGGL((write_kv_kernel<T, 32>), grid, dim3(kTT / P * (32 / P)), 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((write_kv_kernel<T, 64>), grid, dim3(kTT / P * (64 / P)), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((write_kv_kernel<T, 128>), grid, dim3(kTT / P * (128 / P)), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((write_kv_kernel<T, 32, HAS_K>), grid, dim3(kTT / P * (32 / P)), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((write_kv_kernel<T, 64, HAS_K>), grid, dim3(kTT / P * (64 / P)), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((write_kv_kernel<T, 128, HAS_K>), grid, dim3(kTT / P * (128 / P)), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -78,7 +80,9 @@ hipError_t launch_write_kv(const WriteArgs& in, int elt, hipStream_t stream) {
     grid.x = total;
   }
   if (grid.x == 0) return hipSuccess;
-  return elt == 2 ? launch_write_t<uint16_t>(a, grid, stream) : launch_write_t<uint32_t>(a, grid, stream);
+  if (a.k_src)
+    return elt == 2 ? launch_write_t<uint16_t, true>(a, grid, stream) : launch_write_t<uint32_t, true>(a, grid, stream);
+  return elt == 2 ? launch_write_t<uint16_t, false>(a, grid, stream) : launch_write_t<uint32_t, false>(a, grid, stream);
 }
 
 hipError_t launch_vt_to_tok(const WriteArgs& a, int elt, hipStream_t stream) {
