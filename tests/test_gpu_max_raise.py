@@ -1,0 +1,84 @@
+"""GPU parity when a key scores far above the running max of a row.
+
+The bf16 attention kernel starts each row's running max at the largest score of its first half
+tile and raises it only when a half tile's row sum of exponentials passes 2^60 (recomputing that
+half's probabilities and rescaling what was accumulated).  With N(0,1) inputs that never happens,
+so here one history key is planted with a very large dot product against half of the query rows:
+those rows must raise their max in a later tile, and their softmax concentrates on that key.  The
+result is compared with the oracle (fp64 softmax, [LB-fast] "3. KV 缓存 滚动窗口": attention of the
+chunk's queries over the visible cache) on both kernel shapes.
+
+The planted key and queries put all their energy into the lowest-frequency pair of the time part of
+the rotary split, so the rotation changes their dot product by a factor cos(dt * omega) within 1e-5
+of one for the few frames between them.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+from oracle import skv_oracle as so
+from tests import rollout as ro
+
+skv = pytest.importorskip("streaming_kv_cache_amd")
+from streaming_kv_cache_amd.workloads import WORKLOADS  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+A = 40.0  # |planted key| = |planted query|: the score is A^2 / sqrt(D) = 141 (D = 128) or 200 (D = 64)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("name", ["small_abs", "small_rel", "small_d64"])
+def test_hot_key_raises_the_running_max(name, waves, monkeypatch):
+    monkeypatch.setenv("SKV_ATTN_WAVES", waves)
+    wl = WORKLOADS[name]
+    c = wl.cfg
+    f, d = c.tokens_per_frame, c.head_dim
+    say(f"[max raise] {name} waves={waves}")
+    d_t = so.rope_split(d)[0]
+    hot_dim = d_t - 2  # first dim of the lowest-frequency time pair
+    cache = skv.KVCache(c)
+    orc = ro.oracle_for(wl)
+    ro.prefill(wl, cache, orc)
+    n_hist = (c.window_frames - c.sink_frames) // c.chunk_frames + 1  # enough chunks to fill the window
+    hot_row = f // 2  # a token in the middle of the last history chunk's first frame
+    for ch in range(n_hist):
+        t = cache.info().n_appended
+        k = ro.draw(wl, c.chunk_frames, ch, ro.WRITE_BACK, si.K).clone()
+        v = ro.draw(wl, c.chunk_frames, ch, ro.WRITE_BACK, si.V).clone()
+        if ch == n_hist - 1:
+            k[hot_row] = 0
+            k[hot_row, :, hot_dim] = A
+            v[hot_row] = 0.5
+        kd = cache.rope_apply(k.cuda(), start_frame=t) if c.rope_mode == skv.ROPE_ABS else k.cuda()
+        cache.append_evict(kd, v.cuda())
+        orc.append(ro.f64(k), ro.f64(v))
+    if c.rope_mode == skv.ROPE_REL:
+        cache.rope_apply_window()
+    lq = c.chunk_frames * f
+    q = ro.draw(wl, c.chunk_frames, n_hist, 0, si.Q).clone()
+    hot = torch.arange(lq) % 2 == 0  # every other query row looks for the planted key
+    q[hot] = 0
+    q[hot, :, hot_dim] = A
+    k = ro.draw(wl, c.chunk_frames, n_hist, 0, si.K)
+    v = ro.draw(wl, c.chunk_frames, n_hist, 0, si.V)
+    out, _, _ = ro.gpu_pass(cache, q, k, v)
+    torch.cuda.synchronize()
+    ref = orc.chunk_attention(ro.f64(q), ro.f64(k), ro.f64(v))
+    # the planted key takes (almost) all of the weight of the hot rows: they equal its value
+    hot_np = hot.numpy()
+    assert np.abs(ref[hot_np] - 0.5).max() < 1e-6
+    # and the planted key sits past the first tile of the visible keys (the kernel walks the sinks
+    # first, and they fill that tile), so the hot rows start from a small max and must raise it
+    assert c.sink_frames * f >= 64
+    ro.assert_close(out, ref, c.dtype, f"{name} waves={waves}")
+    g = out.float().cpu().double().numpy()
+    assert np.abs(g[hot_np] - 0.5).max() <= 2.0 ** -8
