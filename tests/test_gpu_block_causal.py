@@ -62,6 +62,47 @@ def test_block_causal_small(name, waves, monkeypatch):
     ro.assert_close(got, ref, skv.BF16, f"{name} waves {waves}")
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("name", ["odd_frame", "no_sink", "d64"])
+def test_block_causal_hot_key(name, waves, monkeypatch):
+    """One key of frame 3 scores ~200 (log2 units) against every other query row: rows that see it
+    raise their running max past the first tile (with sinks) or follow it (without), and their
+    output concentrates on its value; all rows stay within the oracle's tolerance.  The key and the
+    queries use only the lowest-frequency time pair, so the rotation keeps their dot product."""
+    monkeypatch.setenv("SKV_ATTN_WAVES", waves)
+    h, d, gh, gw, c, s_, w, n, q0 = CASES[name]
+    say(f"[block-causal hot key] {name} waves={waves}")
+    cfg = skv.Config(h, d, gh, gw, c, s_, w, skv.ROPE_ABS, skv.BF16)
+    f = gh * gw
+    hot_dim = so.rope_split(d)[0] - 2
+    k = si.draw((n * f, h, d), 0, 0, 0, si.K, torch.bfloat16).clone()
+    v = si.draw((n * f, h, d), 0, 0, 0, si.V, torch.bfloat16).clone()
+    q = si.draw(((n - q0) * f, h, d), 0, 0, 0, si.Q, torch.bfloat16).clone()
+    hot_tok = 3 * f + f // 2
+    k[hot_tok] = 0
+    k[hot_tok, :, hot_dim] = 40.0
+    v[hot_tok] = 0.5
+    hot = torch.arange((n - q0) * f) % 2 == 0
+    q[hot] = 0
+    q[hot, :, hot_dim] = 40.0
+    cache = skv.KVCache(cfg)
+    kr = cache.rope_apply(k.cuda(), start_frame=0)
+    qr = cache.rope_apply(q.cuda(), start_frame=q0)
+    out = skv.block_causal_attention(cfg, qr, kr, v.cuda(), q_frame0=q0)
+    torch.cuda.synchronize()
+    kx = so.rope_3d(ro.f64(k), range(n), gh, gw)
+    qx = so.rope_3d(ro.f64(q), range(q0, n), gh, gw)
+    ref = so.block_causal_attention(qx, kx, ro.f64(v), f, c, s_, w, q_frame0=q0)
+    # rows of the query frames that see frame 3 concentrate on the planted value
+    vis = so.block_causal_visible(n, q0, c, s_, w)[:, 3].astype(bool)          # per query frame
+    sees = np.repeat(vis, f) & hot.numpy()
+    assert sees.any()
+    assert np.abs(ref[sees] - 0.5).max() < 1e-6
+    ro.assert_close(out, ref, skv.BF16, f"{name} waves {waves}")
+    g = out.float().cpu().double().numpy()
+    assert np.abs(g[sees] - 0.5).max() <= 2.0 ** -8
+
+
 def test_block_causal_probe_visibility():
     """q = 0 and one-hot values (frame j -> channel j): each output is 1/|visible| on exactly the
     visible frames, which a wrong frame would move by at least 1/W."""
