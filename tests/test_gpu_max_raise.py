@@ -35,14 +35,19 @@ def say(*a):
     sys.stdout.flush()
 
 
+@pytest.mark.parametrize("split", ["0", "1"])
 @pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("name", ["small_abs", "small_rel", "small_d64"])
-def test_hot_key_raises_the_running_max(name, waves, monkeypatch):
+def test_hot_key_raises_the_running_max(name, waves, split, monkeypatch):
+    """split 0: one workgroup walks every key tile of its rows (the max is raised in place); split 1:
+    the keys are split over workgroups (small grids split by default) and the merge pass combines
+    partial results whose maxima differ by ~200 (log2 units)."""
     monkeypatch.setenv("SKV_ATTN_WAVES", waves)
+    monkeypatch.setenv("SKV_ATTN_SPLIT", split)
     wl = WORKLOADS[name]
     c = wl.cfg
     f, d = c.tokens_per_frame, c.head_dim
-    say(f"[max raise] {name} waves={waves}")
+    say(f"[max raise] {name} waves={waves} split={split}")
     d_t = so.rope_split(d)[0]
     hot_dim = d_t - 2  # first dim of the lowest-frequency time pair
     cache = skv.KVCache(c)
@@ -79,6 +84,6 @@ def test_hot_key_raises_the_running_max(name, waves, monkeypatch):
     # and the planted key sits past the first tile of the visible keys (the kernel walks the sinks
     # first, and they fill that tile), so the hot rows start from a small max and must raise it
     assert c.sink_frames * f >= 64
-    ro.assert_close(out, ref, c.dtype, f"{name} waves={waves}")
+    ro.assert_close(out, ref, c.dtype, f"{name} waves={waves} split={split}")
     g = out.float().cpu().double().numpy()
     assert np.abs(g[hot_np] - 0.5).max() <= 2.0 ** -8
