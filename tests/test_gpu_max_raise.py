@@ -6,7 +6,8 @@ half's probabilities and rescaling what was accumulated).  With N(0,1) inputs th
 so here one history key is planted with a very large dot product against half of the query rows:
 those rows must raise their max in a later tile, and their softmax concentrates on that key.  The
 result is compared with the oracle (fp64 softmax, [LB-fast] "3. KV 缓存 滚动窗口": attention of the
-chunk's queries over the visible cache) on both kernel shapes.
+chunk's queries over the visible cache) on both kernel shapes, and for the fp32 kernel (which
+follows the max over every 16 keys; the wave-count setting does not apply to it).
 
 The planted key and queries put all their energy into the lowest-frequency pair of the time part of
 the rotary split, so the rotation changes their dot product by a factor cos(dt * omega) within 1e-5
@@ -37,7 +38,7 @@ def say(*a):
 
 @pytest.mark.parametrize("split", ["0", "1"])
 @pytest.mark.parametrize("waves", ["4", "8"])
-@pytest.mark.parametrize("name", ["small_abs", "small_rel", "small_d64"])
+@pytest.mark.parametrize("name", ["small_abs", "small_rel", "small_d64", "small_f32_rel"])
 def test_hot_key_raises_the_running_max(name, waves, split, monkeypatch):
     """split 0: one workgroup walks every key tile of its rows (the max is raised in place); split 1:
     the keys are split over workgroups (small grids split by default) and the merge pass combines
@@ -81,9 +82,11 @@ def test_hot_key_raises_the_running_max(name, waves, split, monkeypatch):
     # the planted key takes (almost) all of the weight of the hot rows: they equal its value
     hot_np = hot.numpy()
     assert np.abs(ref[hot_np] - 0.5).max() < 1e-6
-    # and the planted key sits past the first tile of the visible keys (the kernel walks the sinks
-    # first, and they fill that tile), so the hot rows start from a small max and must raise it
-    assert c.sink_frames * f >= 64
+    # and, for the bf16 kernel, the planted key sits past the first tile of the visible keys (the
+    # kernel walks the sinks first, and they fill that tile), so the hot rows start from a small max
+    # and must raise it (the fp32 kernel follows the max over every 16 keys)
+    if c.dtype == skv.BF16:
+        assert c.sink_frames * f >= 64
     ro.assert_close(out, ref, c.dtype, f"{name} waves={waves} split={split}")
     g = out.float().cpu().double().numpy()
-    assert np.abs(g[hot_np] - 0.5).max() <= 2.0 ** -8
+    assert np.abs(g[hot_np] - 0.5).max() <= (2.0 ** -8 if c.dtype == skv.BF16 else 1e-6)
