@@ -85,6 +85,75 @@ def box_peak(torch):
     return {"cus": cus, "sclk_mhz": khz.value / 1e3, "tflops": round(cus * 4096 * khz.value * 1e3 / 1e12, 1)}
 
 
+class GpuClock:
+    """The GPU's graphics clock and socket power, read every 5 ms on a host thread through amdsmi
+    (read-only device metrics) while a stretch of work runs.  Boxes of the same model hold different
+    clocks under this load, which is most of the spread of the kernel times between them.  Every
+    figure is None where amdsmi is missing, refuses, or cannot tell which device torch uses."""
+
+    def __init__(self, torch):
+        self.samples, self.handle, self.smi = [], None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            props = torch.cuda.get_device_properties(torch.cuda.current_device())
+            bus = getattr(props, "pci_bus_id", None)
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)        # "dddd:bb:dd.f"
+                if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                    self.handle = h
+            if self.handle is None and len(handles) == 1:
+                self.handle = handles[0]
+            self.smi = amdsmi
+            if self.handle is not None:
+                amdsmi.amdsmi_get_gpu_metrics_info(self.handle)   # the first read is slow: not in the window
+        except Exception:
+            self.handle = None
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+                    self.samples.append((time.perf_counter(), float(m["current_gfxclk"]),
+                                         float(m["current_socket_power"])))
+                except Exception:
+                    pass
+                self._stop.wait(0.005)
+        if self.handle is not None:
+            self._thread = threading.Thread(target=run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.handle is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def span(self):
+        return self.samples[-1][0] - self.samples[0][0] if len(self.samples) > 1 else 0.0
+
+    def summary(self, what):
+        # the device refreshes these metrics slowly: only the second half of the window counts
+        if self.span() < 0.5:
+            return None
+        t_half = self.samples[0][0] + 0.5 * self.span()
+        late = [x for x in self.samples if x[0] >= t_half and x[1] > 500.0]
+        if not late:
+            return None
+        clk = np.array([x[1] for x in late])
+        pw = np.array([x[2] for x in late])
+        return {"gfxclk_mhz": round(float(np.median(clk)), 0),
+                "gfxclk_mhz_p10_p90": [round(float(np.percentile(clk, 10)), 0), round(float(np.percentile(clk, 90)), 0)],
+                "socket_power_w": round(float(np.median(pw)), 0), "samples": len(late),
+                "window_s": round(self.span(), 2), "during": what}
+
+
 def kernel_sha(name: str) -> str:
     """Hash of a kernel source and of the library headers it includes, each with its comments and
     whitespace removed: counters taken on the code stay valid across comment edits, and any change to
@@ -547,13 +616,27 @@ def main():
         mem["max_allocated_MB"] = round(torch.cuda.max_memory_allocated() / 2**20, 1)
     _, steps_ms = avg_ms(r.ev, "step0", "step1")
     ms_step = wall * 1e3 / args.steps
-    # the same number of steps (at most 20) again with an event pair around every kernel
+    # the same number of steps (at most 20) again with an event pair around every kernel, the GPU's
+    # clock sampled meanwhile
     r.ev = {k: [] for k in ev_kinds}
     r.kernel_events = True
-    for _ in range(min(args.steps, 20)):
-        r.step()
-    torch.cuda.synchronize()
+    clock = GpuClock(torch)
+    with clock:
+        for _ in range(min(args.steps, 20)):
+            r.step()
+        torch.cuda.synchronize()
     ev = r.ev
+    clock_what = "the instrumented steps"
+    if clock.handle is not None and clock.span() < 1.0:
+        # a short pass: more steps of the same schedule (not timed, no events) until the clock has
+        # been watched for a second
+        r.ev = None
+        clock_what = "the instrumented steps and further untimed steps, one second in all"
+        t_end = time.perf_counter() + 2.0
+        with clock:
+            while clock.span() < 1.0 and time.perf_counter() < t_end:
+                r.step()
+                torch.cuda.synchronize()
     if args.calibrate:
         r.caches[0].gather()   # K rows: n_cached*F*H*D elements read and written by copy_frames_kernel
         torch.cuda.synchronize()
@@ -613,7 +696,13 @@ def main():
         "per_chunk_ms": {"mean": round(float(np.mean(steps_ms)), 4), "p50": round(float(np.median(steps_ms)), 4),
                          "p99": round(float(np.percentile(steps_ms, 99)), 4),
                          "instrumented_mean": round(float(np.mean(steps_ms_instr)), 4)},
+        "gpu_clock": clock.summary(clock_what),
     }
+    if out["gpu_clock"] and bf16:
+        # the same attention rate against the peak scaled to the clock this box held meanwhile
+        # (the published peak is quoted at 2400 MHz)
+        out["chunk_attention"]["frac_of_peak_at_held_clock"] = round(
+            attn_tflops / (peak * out["gpu_clock"]["gfxclk_mhz"] / 2400.0), 4)
     stage_bytes = 2 * lq * h * d * elt                        # V read, V^T written
     if r.fused:
         out["chunk_attention"]["note"] = ("fused rotation: includes the launch that rotates q / k and stages V "
